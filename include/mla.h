@@ -1,0 +1,176 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) MLA latent-cache decode library.
+ *
+ * Multi-head latent attention decode in the absorbed ("MQA") form:
+ *
+ *   1. mla_absorb_q          q_abs[n][h] = [ W_UK[h]^T q_nope[n][h] | q_pe[n][h] ]
+ *   2. mla_decode_attention  split-KV attention of every absorbed query over the
+ *                            shared paged latent cache rows [c_kv | k_pe], values
+ *                            = the leading kv_rank columns of the same rows, then
+ *                            an LSE-weighted merge of the splits
+ *   3. mla_decompress_v      out[n][h] = W_UV[h] o_lat[n][h]
+ *
+ * Pages this interface follows (cited by title and section):
+ *   memra-engine 0.124.0 source page "mla.rs": MlaDims (geometry), MlaDims::scale,
+ *     MlaInputs (layouts and the causal suffix rule), mla_attend_absorbed.
+ *   vllm.cpp source page "cpu_mla_attn.cpp": MlaDecodeAttentionKernel (argument
+ *     list, paged addressing, LSE definition, zeros for an empty request).
+ *   vLLM API page "vllm.v1.attention.backends.mla.cpu_mla": CPUMLABackend (head
+ *     size 576 = 512 + 64, block size 16), CPUMLAImpl.forward_mqa (decode call).
+ *   CANN page "aclnnMlaProlog": two-phase call (workspace size, then execute).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     never allocates, frees or keeps a tensor.  Layouts are contiguous,
+ *     row-major, exactly as stated per argument.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work and return; buffers must stay valid and unmodified until the stream
+ *     reaches that point.
+ *   - Outputs are fully overwritten (no pre-zeroing needed).  Outputs and the
+ *     workspace must not alias each other or any input.
+ *   - Every function returns an mla_status; nothing aborts or throws.  A
+ *     host-detected error returns before anything is enqueued and leaves all
+ *     outputs untouched.
+ *   - mla_dtype gives the storage type of a tensor: IEEE float32 or bfloat16.
+ */
+#ifndef MLA_LATENT_CACHE_AMD_MLA_H
+#define MLA_LATENT_CACHE_AMD_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Head geometry (memra mla.rs, struct MlaDims): n_head query heads, query-key
+ * width d_nope (no rope) + d_rope (rope), decompressed value width d_v, latent
+ * rank kv_rank.  A latent cache row is kv_rank + d_rope wide.
+ * GLM-5.2: {64, 192, 64, 256, 512}; NoPE geometry: {64, 256, 0, 256, 512}. */
+typedef struct mla_dims {
+  int32_t n_head;
+  int32_t d_nope;
+  int32_t d_rope;
+  int32_t d_v;
+  int32_t kv_rank;
+} mla_dims;
+
+typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  MLA_ERR_DIMS = 2,        /* a geometry field is out of range             */
+  MLA_ERR_SHAPE = 3,       /* a size argument is out of range              */
+  MLA_ERR_UNSUPPORTED = 4, /* valid request this library does not handle   */
+  MLA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required   */
+  MLA_ERR_HIP = 6,         /* the HIP runtime reported an error            */
+  MLA_ERR_ARG = 7          /* other invalid argument (scale, dtype code)   */
+} mla_status;
+
+/* Bits of the device-detected data-error word (mla_decode_status).  A request
+ * that trips one gets NaN in every output element and LSE of that request. */
+#define MLA_DATA_NEG_LEN 0x1u        /* seq_lens[b] < 0                            */
+#define MLA_DATA_LEN_OVER_TABLE 0x2u /* seq_lens[b] > max_blocks * block_size      */
+#define MLA_DATA_LEN_BELOW_TQ 0x4u   /* 0 < seq_lens[b] < t_q                      */
+#define MLA_DATA_BAD_BLOCK 0x8u      /* a needed block id is outside [0,num_blocks) */
+
+/* Softmax scale of the geometry: 1 / sqrt(d_nope + d_rope), the original
+ * query-key head width, not the absorbed width (memra mla.rs, MlaDims::scale).
+ * Returns NaN for a NULL pointer or d_nope + d_rope < 1. */
+float mla_default_scale(const mla_dims* dims);
+
+/* Step 1: absorb the query through W_UK (memra mla.rs, mla_attend_absorbed,
+ * absorb step; CANN aclnnMlaProlog, the q^N = q^C W^UK formula) and append
+ * the rope part (vLLM cpu_mla, forward_mqa concatenation):
+ *   q_abs[n][h][l]           = sum_p q_nope[n][h][p] * w_uk[h][p][l]   l < kv_rank
+ *   q_abs[n][h][kv_rank + r] = q_pe[n][h][r]                            r < d_rope
+ * q_nope [n_tok][n_head][d_nope], q_pe [n_tok][n_head][d_rope] (may be NULL
+ * when d_rope == 0), w_uk [n_head][d_nope][kv_rank]: all of type in_dt.
+ * q_abs  [n_tok][n_head][kv_rank + d_rope] of type out_dt.
+ * Products accumulate in float32.  n_tok == 0 is a no-op.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DIMS (n_head, d_nope, kv_rank < 1 or d_rope < 0),
+ * MLA_ERR_SHAPE (n_tok < 0), MLA_ERR_ARG (bad dtype code), MLA_ERR_HIP. */
+mla_status mla_absorb_q(const mla_dims* dims, int64_t n_tok, const void* q_nope,
+                        const void* q_pe, const void* w_uk, mla_dtype in_dt, void* q_abs,
+                        mla_dtype out_dt, void* stream);
+
+/* Phase one of decode (CANN two-phase convention): bytes of device workspace
+ * that mla_decode_attention needs for these sizes.  num_splits is the number
+ * of KV splits per request (0 = choose automatically for the current device).
+ * Errors: MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED
+ * (block_size != 16), MLA_ERR_HIP (device query failed, auto mode only). */
+mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t t_q,
+                                     int32_t max_blocks, int32_t block_size,
+                                     int32_t num_splits, size_t* bytes);
+
+/* The number of KV splits per request mla_decode_attention will use for these
+ * sizes (resolves num_splits == 0).  Returns 0 on invalid arguments. */
+int32_t mla_decode_resolve_splits(const mla_dims* dims, int32_t batch, int32_t t_q,
+                                  int32_t max_blocks, int32_t num_splits);
+
+/* Step 2: paged decode attention over the latent cache (vllm.cpp
+ * cpu_mla_attn.cpp, MlaDecodeAttentionKernel; memra mla.rs, MlaInputs causal
+ * rule), computed as split-KV partial attention plus an LSE-weighted merge.
+ *
+ * Semantics, per request b, query i < t_q, head h:
+ *   L = seq_lens[b] counts every cache row of the request INCLUDING its t_q
+ *   query rows; query i sees rows 0 .. L - t_q + i (for t_q == 1: all L rows).
+ *   Row j of request b is kv_cache[block_table[b][j / 16]][j % 16][0 .. D),
+ *   D = kv_rank + d_rope, laid out [c_kv | k_pe].
+ *   s_j   = scale * <q_abs[b][i][h], row_j>           (all D columns)
+ *   o_lat = sum_j softmax(s)_j * row_j[0 .. kv_rank)  (values = leading kv_rank)
+ *   lse   = natural log of sum_j exp(s_j)              (scaled logits)
+ *   L == 0: o_lat = 0 and lse = -inf for every query and head.
+ *
+ * q_abs     [batch][t_q][n_head][D], type dt
+ * kv_cache  [num_blocks][block_size][D], type dt (d_nope and d_v are unused)
+ * block_table int32 [batch][max_blocks]; entries past a request's last block
+ *           are never read
+ * seq_lens  int32 [batch]
+ * out_lat   [batch][t_q][n_head][kv_rank], type out_dt
+ * lse       float32 [batch][t_q][n_head], or NULL
+ * workspace device buffer of at least mla_decode_workspace_size() bytes for
+ *           the same (dims, batch, t_q, max_blocks, block_size, num_splits);
+ *           it also holds the data-error word read by mla_decode_status.
+ * Results do not depend on the block labels; for a fixed num_splits they are
+ * bitwise reproducible run to run.  Accumulation is float32 (bf16 products).
+ * Errors: MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE (batch < 0, t_q < 1,
+ * max_blocks < 1, num_blocks < 1, num_splits < 0), MLA_ERR_UNSUPPORTED
+ * (block_size != 16), MLA_ERR_ARG (scale not finite or <= 0, bad dtype code),
+ * MLA_ERR_WORKSPACE, MLA_ERR_HIP.  Data errors found on the device (see the
+ * MLA_DATA_* bits) do not fail the call: they poison that request's outputs
+ * with NaN and are reported by mla_decode_status. */
+mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch, int32_t t_q,
+                                const void* q_abs, const void* kv_cache, mla_dtype dt,
+                                int64_t num_blocks, int32_t block_size,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_lens, void* out_lat, mla_dtype out_dt,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                int32_t num_splits, void* stream);
+
+/* Step 3: decompress the latent output once through W_UV (memra mla.rs,
+ * mla_attend_absorbed, decompress step):
+ *   out[n][h][j] = sum_l w_uv[h][j][l] * o_lat[n][h][l]
+ * o_lat [n_tok][n_head][kv_rank] type o_dt, w_uv [n_head][d_v][kv_rank] type
+ * w_dt, out [n_tok][n_head][d_v] type out_dt.  Float32 accumulation.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DIMS (n_head, d_v, kv_rank < 1), MLA_ERR_SHAPE
+ * (n_tok < 0), MLA_ERR_ARG, MLA_ERR_HIP. */
+mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_lat,
+                            mla_dtype o_dt, const void* w_uv, mla_dtype w_dt, void* out,
+                            mla_dtype out_dt, void* stream);
+
+/* Waits for `stream`, then ORs the MLA_DATA_* bits that the most recent
+ * mla_decode_attention call on this workspace recorded into *flags (0 = no
+ * data error).  Errors: MLA_ERR_NULL, MLA_ERR_WORKSPACE (the workspace holds
+ * no completed decode), MLA_ERR_HIP. */
+mla_status mla_decode_status(const void* workspace, uint32_t* flags, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_string(mla_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LATENT_CACHE_AMD_MLA_H */

@@ -1,0 +1,30 @@
+"""MI355X (gfx950) MLA latent-cache decode: C-ABI library + thin binding.
+
+The hot path is three library calls, each a hand-written HIP kernel set:
+``mla_absorb_q`` (fold W_UK into the query), ``mla_decode_attention`` (split-KV
+attention over the paged latent cache plus the LSE-weighted merge) and
+``mla_decompress_v`` (one W_UV decompression).  See include/mla.h for the
+contract of every entry point.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    MLA_BF16,
+    MLA_DATA_BAD_BLOCK,
+    MLA_DATA_LEN_BELOW_TQ,
+    MLA_DATA_LEN_OVER_TABLE,
+    MLA_DATA_NEG_LEN,
+    MLA_F32,
+    MlaError,
+    as_dims,
+    lib,
+    mla_absorb_q,
+    mla_decode_attention,
+    mla_decode_resolve_splits,
+    mla_decode_status,
+    mla_decode_workspace_size,
+    mla_decompress_v,
+    mla_default_scale,
+    mla_dims,
+    mla_status_string,
+)

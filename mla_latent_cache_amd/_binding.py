@@ -1,0 +1,188 @@
+"""ctypes binding of libmla_amd.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (include/mla.h)
+and does nothing but turn torch tensors into pointers, sizes and dtype codes,
+call the library, and raise MlaError on a non-zero status.  All computation
+happens in the HIP kernels behind the C ABI; torch only owns device memory and
+streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_amd.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE = 0, 1, 2, 3
+MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP, MLA_ERR_ARG = 4, 5, 6, 7
+MLA_DATA_NEG_LEN, MLA_DATA_LEN_OVER_TABLE, MLA_DATA_LEN_BELOW_TQ, MLA_DATA_BAD_BLOCK = 1, 2, 4, 8
+
+EXPORTS = ("mla_default_scale", "mla_absorb_q", "mla_decode_workspace_size",
+           "mla_decode_resolve_splits", "mla_decode_attention", "mla_decompress_v",
+           "mla_decode_status", "mla_status_string")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_text(status)})")
+        self.status = status
+
+
+class mla_dims(ctypes.Structure):
+    _fields_ = [("n_head", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("kv_rank", ctypes.c_int32)]
+
+
+DimsLike = Union[mla_dims, Sequence[int], object]
+
+_LIB = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback exists)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m mla_latent_cache_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz, f32, vp = (ctypes.POINTER(mla_dims), ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p)
+    L.mla_default_scale.restype = f32
+    L.mla_default_scale.argtypes = [P]
+    L.mla_absorb_q.restype = ctypes.c_int
+    L.mla_absorb_q.argtypes = [P, i64, vp, vp, vp, ctypes.c_int, vp, ctypes.c_int, vp]
+    L.mla_decode_workspace_size.restype = ctypes.c_int
+    L.mla_decode_workspace_size.argtypes = [P, i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.mla_decode_resolve_splits.restype = i32
+    L.mla_decode_resolve_splits.argtypes = [P, i32, i32, i32, i32]
+    L.mla_decode_attention.restype = ctypes.c_int
+    L.mla_decode_attention.argtypes = [P, f32, i32, i32, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
+                                       vp, ctypes.c_int, vp, vp, sz, i32, vp]
+    L.mla_decompress_v.restype = ctypes.c_int
+    L.mla_decompress_v.argtypes = [P, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp]
+    L.mla_decode_status.restype = ctypes.c_int
+    L.mla_decode_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_status_string.argtypes = [ctypes.c_int]
+    _LIB = L
+    return L
+
+
+def status_text(code: int) -> str:
+    try:
+        return lib().mla_status_string(int(code)).decode()
+    except Exception:  # library missing: still give a readable message
+        return "unknown"
+
+
+def as_dims(d: DimsLike) -> mla_dims:
+    if isinstance(d, mla_dims):
+        return d
+    if isinstance(d, (tuple, list)):
+        return mla_dims(*[int(x) for x in d])
+    return mla_dims(int(d.n_head), int(d.d_nope), int(d.d_rope), int(d.d_v), int(d.kv_rank))
+
+
+def _check(fn: str, st: int) -> None:
+    if st != MLA_OK:
+        raise MlaError(fn, st)
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the MLA library must be device tensors")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MLA library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def mla_default_scale(dims: DimsLike) -> float:
+    d = as_dims(dims)
+    return float(lib().mla_default_scale(ctypes.byref(d)))
+
+
+def mla_absorb_q(dims: DimsLike, q_nope, q_pe, w_uk, q_abs, stream=None) -> None:
+    """q_abs[n][h] = [W_UK[h]^T q_nope[n][h] | q_pe[n][h]]; shapes as in include/mla.h."""
+    d = as_dims(dims)
+    n_tok = q_nope.numel() // max(1, d.n_head * d.d_nope)
+    pe = q_pe if (q_pe is not None and q_pe.numel() > 0) else None
+    _check("mla_absorb_q", lib().mla_absorb_q(ctypes.byref(d), n_tok, _ptr(q_nope), _ptr(pe), _ptr(w_uk),
+                                               _dt(q_nope), _ptr(q_abs), _dt(q_abs), _stream(stream)))
+
+
+def mla_decode_workspace_size(dims: DimsLike, batch: int, t_q: int, max_blocks: int,
+                              block_size: int = 16, num_splits: int = 0) -> int:
+    d = as_dims(dims)
+    out = ctypes.c_size_t(0)
+    _check("mla_decode_workspace_size",
+           lib().mla_decode_workspace_size(ctypes.byref(d), batch, t_q, max_blocks, block_size, num_splits,
+                                           ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_decode_resolve_splits(dims: DimsLike, batch: int, t_q: int, max_blocks: int,
+                              num_splits: int = 0) -> int:
+    d = as_dims(dims)
+    return int(lib().mla_decode_resolve_splits(ctypes.byref(d), batch, t_q, max_blocks, num_splits))
+
+
+def mla_decode_attention(dims: DimsLike, scale: float, q_abs, kv_cache, block_table, seq_lens, out_lat,
+                         lse=None, workspace=None, num_splits: int = 0, stream=None) -> None:
+    """Paged split-KV decode attention.  q_abs [B][t_q][H][D], kv_cache
+    [num_blocks][16][D], block_table int32 [B][max_blocks], seq_lens int32 [B],
+    out_lat [B][t_q][H][kv_rank], lse float32 [B][t_q][H] or None, workspace a
+    uint8 device tensor of at least mla_decode_workspace_size() bytes."""
+    d = as_dims(dims)
+    B, t_q = int(q_abs.shape[0]), int(q_abs.shape[1])
+    if workspace is None:
+        raise ValueError("mla_decode_attention needs a workspace tensor")
+    _check("mla_decode_attention", lib().mla_decode_attention(
+        ctypes.byref(d), float(scale), B, t_q, _ptr(q_abs), _ptr(kv_cache), _dt(kv_cache),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]),
+        _ptr(seq_lens), _ptr(out_lat), _dt(out_lat), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), int(num_splits), _stream(stream)))
+
+
+def mla_decompress_v(dims: DimsLike, o_lat, w_uv, out, stream=None) -> None:
+    """out[n][h][j] = sum_l W_UV[h][j][l] o_lat[n][h][l]."""
+    d = as_dims(dims)
+    n_tok = o_lat.numel() // max(1, d.n_head * d.kv_rank)
+    _check("mla_decompress_v", lib().mla_decompress_v(ctypes.byref(d), n_tok, _ptr(o_lat), _dt(o_lat),
+                                                       _ptr(w_uv), _dt(w_uv), _ptr(out), _dt(out),
+                                                       _stream(stream)))
+
+
+def mla_decode_status(workspace, stream=None) -> int:
+    """MLA_DATA_* bits recorded by the last decode on this workspace (waits for the stream)."""
+    flags = ctypes.c_uint32(0)
+    _check("mla_decode_status", lib().mla_decode_status(_ptr(workspace), ctypes.byref(flags), _stream(stream)))
+    return int(flags.value)
+
+
+def mla_status_string(code: int) -> str:
+    return lib().mla_status_string(int(code)).decode()

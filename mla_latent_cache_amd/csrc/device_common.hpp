@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Buffer-resource word 3 for raw (unswizzled, untyped) 32-bit-indexed access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// bfloat16 bits -> float (exact widening).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two floats -> packed pair of bfloat16 (RNE) in one dword, lo = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Reinterpret four dwords as eight bfloat16 MFMA operand lanes.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+template <typename T>
+struct Storage;
+
+template <>
+struct Storage<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+
+template <>
+struct Storage<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+// 16 x 16 x 32 bf16 matrix-core product, float32 accumulate.
+// Lane l: A row l%16, k = 8*(l/16)..+7; B column l%16, same k; C rows 4*(l/16)+i, column l%16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16-lane group, lane j receives, as element e,
+// the 16-bit word (j % 4) of the 8 bytes addressed by lane 4*e + j/4 of its group.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_byte_addr));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+}
+
+// 16 bytes from buffer offset `voff` straight into LDS at (wave base + 16 * lane).
+// Offsets at or beyond the buffer size deliver zeros.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds_wave_base,
+                                                  uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_wave_base), 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace mla

@@ -1,0 +1,255 @@
+// Per-head batched GEMMs around the latent attention, for gfx950.
+//
+// Absorb (memra-engine "mla.rs", mla_attend_absorbed absorb step; CANN
+// "aclnnMlaProlog", the q^N = q^C W^UK formula; vLLM "cpu_mla",
+// forward_mqa query concatenation):
+//   q_abs[n][h][l] = sum_p q_nope[n][h][p] * W_UK[h][p][l],  q_abs[n][h][kv_rank:] = q_pe[n][h]
+// Decompress (memra-engine "mla.rs", mla_attend_absorbed decompress step):
+//   out[n][h][j] = sum_l W_UV[h][j][l] * o_lat[n][h][l]
+//
+// Both are weight-read bound at decode batch sizes (a few to a few hundred
+// tokens against 12-17 MB of weights), so each weight element is read from
+// HBM exactly once: one workgroup owns one head and a 64-column slice of the
+// weight, keeps that slice on chip, and sweeps every token past it with
+// 16x16x32 bf16 MFMA.  W_UV rows are contiguous along the contraction index,
+// so its B operand is loaded straight into VGPRs; W_UK is contiguous along the
+// output index, so its slice is staged in LDS and read back with the
+// transposing ds_read_b64_tr_b16.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int kCols = 64;  // weight columns per workgroup (16 per wave)
+
+// Load 8 consecutive activations starting at p as bf16 MFMA operand lanes.
+__device__ __forceinline__ bf16x8 load8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 load8(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  const u32x4 v = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                   pack_bf16x2(b[2], b[3])};
+  return as_bf16x8(v);
+}
+
+template <typename TO>
+__device__ __forceinline__ void store_c(TO* out, int64_t idx, float v) { Storage<TO>::store(out, idx, v); }
+
+// ---------------------------------------------------------------------------
+// Absorb, bf16 in.  Grid (n_head, kv_rank / 64); 256 threads.  DN = d_nope (multiple of 32).
+// W_UK[h][0:DN][c0:c0+64] is staged in LDS with a 160-byte row pitch (40 dwords = 8 * odd).
+// ---------------------------------------------------------------------------
+template <typename TO>
+__global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_rank, int64_t n_tok,
+                                                   const uint16_t* __restrict__ q_nope,
+                                                   const uint16_t* __restrict__ q_pe,
+                                                   const uint16_t* __restrict__ w_uk,
+                                                   TO* __restrict__ q_abs) {
+  constexpr int PITCH = 80;  // elements per LDS row (64 used)
+  extern __shared__ __attribute__((aligned(16))) uint16_t wl[];  // [DN][PITCH]
+  const int h = blockIdx.x, c0 = blockIdx.y * kCols;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int D = kv_rank + R;
+
+  // Stage the weight slice: DN rows x 128 bytes, 16 bytes per thread per step.
+  const uint16_t* wsrc = w_uk + (int64_t)h * DN * kv_rank + c0;
+  for (int idx = tid; idx < DN * 8; idx += 256) {
+    const int p = idx >> 3, c = (idx & 7) * 8;
+    *reinterpret_cast<u32x4*>(wl + p * PITCH + c) = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)p * kv_rank + c);
+  }
+  __syncthreads();
+
+  // The rope tail is copied once per (token, head) by the first column slice.
+  if (blockIdx.y == 0) {
+    for (int64_t idx = tid; idx < n_tok * R; idx += 256) {
+      const int64_t n = idx / R;
+      const int r = (int)(idx - n * R);
+      store_c(q_abs, (n * H + h) * D + kv_rank + r, bf16_to_f32(q_pe[(n * H + h) * R + r]));
+    }
+  }
+
+  // This wave's 16 columns; B operand rows (p) read transposed from LDS.
+  const int cw = w * 16;
+  const int ksteps = DN / 32;
+  for (int64_t m0 = 0; m0 < n_tok; m0 += 16) {
+    const int64_t n_a = m0 + l16;  // A-operand token of this lane
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < ksteps; ++t) {
+      const bf16x8 A = n_a < n_tok ? load8(q_nope + (n_a * H + h) * DN + 32 * t + 8 * g) : zero_bf16x8();
+      // rows p0 .. p0+3 and p0+4 .. p0+7 at columns cw .. cw+15
+      const int p0 = 32 * t + 8 * g;
+      const int prow = p0 + (l16 >> 2);
+      const int col = cw + 4 * (l16 & 3);
+      const s16x4 b0 = lds_read_tr16(wl + prow * PITCH + col);
+      const s16x4 b1 = lds_read_tr16(wl + (prow + 4) * PITCH + col);
+      const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc = mfma16x16x32(A, B, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = m0 + 4 * g + i;
+      if (n < n_tok) store_c(q_abs, (n * H + h) * D + c0 + cw + l16, acc[i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decompress, bf16 weights.  Grid (n_head, d_v / 64); 256 threads; kv_rank = KR
+// (multiple of 32, at most 512).  Each wave keeps its 16 weight rows in VGPRs.
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void decompress_mfma(int H, int DV, int KR, int64_t n_tok,
+                                                       const TI* __restrict__ o_lat,
+                                                       const uint16_t* __restrict__ w_uv,
+                                                       TO* __restrict__ out) {
+  constexpr int MAXK = 16;  // up to 512 / 32 contraction steps
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int j_b = blockIdx.y * kCols + w * 16 + l16;  // B-operand column (output index) of this lane
+  const int ksteps = KR / 32;
+  bf16x8 Bk[MAXK];
+  const uint16_t* wrow = w_uv + ((int64_t)h * DV + j_b) * KR + 8 * g;
+#pragma unroll
+  for (int t = 0; t < MAXK; ++t)
+    Bk[t] = (t < ksteps && j_b < DV) ? load8(wrow + 32 * t) : zero_bf16x8();
+  const int jc = blockIdx.y * kCols + w * 16 + l16;  // C-operand column
+  for (int64_t m0 = 0; m0 < n_tok; m0 += 16) {
+    const int64_t n_a = m0 + l16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < MAXK; ++t) {
+      if (t < ksteps) {
+        const bf16x8 A = n_a < n_tok ? load8(o_lat + (n_a * H + h) * KR + 32 * t + 8 * g) : zero_bf16x8();
+        acc = mfma16x16x32(A, Bk[t], acc);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t n = m0 + 4 * g + i;
+      if (n < n_tok && jc < DV) store_c(out, (n * H + h) * DV + jc, acc[i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic fallbacks (any sizes, float32 or bf16 storage): one thread per output.
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void absorb_generic(int H, int DN, int R, int KR, int64_t n_tok,
+                                                      const TI* q_nope, const TI* q_pe, const TI* w_uk,
+                                                      TO* q_abs) {
+  const int D = KR + R;
+  const int64_t total = n_tok * H * D;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t nh = idx / D;
+    const int c = (int)(idx - nh * D);
+    const int h = (int)(nh % H);
+    float v;
+    if (c < KR) {
+      v = 0.f;
+      for (int p = 0; p < DN; ++p)
+        v += Storage<TI>::load(q_nope, nh * DN + p) * Storage<TI>::load(w_uk, ((int64_t)h * DN + p) * KR + c);
+    } else {
+      v = Storage<TI>::load(q_pe, nh * R + (c - KR));
+    }
+    store_c(q_abs, idx, v);
+  }
+}
+
+template <typename TI, typename TW, typename TO>
+__global__ __launch_bounds__(256) void decompress_generic(int H, int DV, int KR, int64_t n_tok,
+                                                          const TI* o_lat, const TW* w_uv, TO* out) {
+  const int64_t total = n_tok * H * DV;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
+    const int64_t nh = idx / DV;
+    const int j = (int)(idx - nh * DV);
+    const int h = (int)(nh % H);
+    float v = 0.f;
+    for (int l = 0; l < KR; ++l)
+      v += Storage<TW>::load(w_uv, ((int64_t)h * DV + j) * KR + l) * Storage<TI>::load(o_lat, nh * KR + l);
+    store_c(out, idx, v);
+  }
+}
+
+unsigned generic_grid(int64_t total) {
+  int64_t g = (total + 255) / 256;
+  if (g > 65536) g = 65536;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_absorb(int H, int DN, int R, int KR, int64_t n_tok, const void* q_nope, const void* q_pe,
+                         const void* w_uk, bool in_bf16, void* q_abs, bool out_bf16, hipStream_t stream) {
+  if (n_tok == 0) return hipSuccess;
+  const bool mfma = in_bf16 && DN % 32 == 0 && KR % kCols == 0 && DN <= 512;
+  if (mfma) {
+    const dim3 grid(H, KR / kCols);
+    const size_t lds = (size_t)DN * 80 * 2;
+    const uint16_t *qn = static_cast<const uint16_t*>(q_nope), *qp = static_cast<const uint16_t*>(q_pe),
+                   *wk = static_cast<const uint16_t*>(w_uk);
+    if (out_bf16)
+      hipLaunchKernelGGL(absorb_mfma<uint16_t>, grid, dim3(256), lds, stream, H, DN, R, KR, n_tok, qn, qp, wk,
+                         static_cast<uint16_t*>(q_abs));
+    else
+      hipLaunchKernelGGL(absorb_mfma<float>, grid, dim3(256), lds, stream, H, DN, R, KR, n_tok, qn, qp, wk,
+                         static_cast<float*>(q_abs));
+    return hipGetLastError();
+  }
+  const unsigned grid = generic_grid(n_tok * H * (KR + R));
+  if (in_bf16) {
+    const uint16_t *qn = static_cast<const uint16_t*>(q_nope), *qp = static_cast<const uint16_t*>(q_pe),
+                   *wk = static_cast<const uint16_t*>(w_uk);
+    if (out_bf16)
+      hipLaunchKernelGGL((absorb_generic<uint16_t, uint16_t>), dim3(grid), dim3(256), 0, stream, H, DN, R, KR,
+                         n_tok, qn, qp, wk, static_cast<uint16_t*>(q_abs));
+    else
+      hipLaunchKernelGGL((absorb_generic<uint16_t, float>), dim3(grid), dim3(256), 0, stream, H, DN, R, KR,
+                         n_tok, qn, qp, wk, static_cast<float*>(q_abs));
+  } else {
+    const float *qn = static_cast<const float*>(q_nope), *qp = static_cast<const float*>(q_pe),
+                *wk = static_cast<const float*>(w_uk);
+    if (out_bf16)
+      hipLaunchKernelGGL((absorb_generic<float, uint16_t>), dim3(grid), dim3(256), 0, stream, H, DN, R, KR,
+                         n_tok, qn, qp, wk, static_cast<uint16_t*>(q_abs));
+    else
+      hipLaunchKernelGGL((absorb_generic<float, float>), dim3(grid), dim3(256), 0, stream, H, DN, R, KR, n_tok,
+                         qn, qp, wk, static_cast<float*>(q_abs));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decompress(int H, int DV, int KR, int64_t n_tok, const void* o_lat, bool o_bf16,
+                             const void* w_uv, bool w_bf16, void* out, bool out_bf16, hipStream_t stream) {
+  if (n_tok == 0) return hipSuccess;
+  const bool mfma = w_bf16 && KR % 32 == 0 && KR <= 512;
+  if (mfma) {
+    const dim3 grid(H, (DV + kCols - 1) / kCols);
+    const uint16_t* wv = static_cast<const uint16_t*>(w_uv);
+#define MLA_DECOMP(TI, TO)                                                                               \
+  hipLaunchKernelGGL((decompress_mfma<TI, TO>), grid, dim3(256), 0, stream, H, DV, KR, n_tok,              \
+                     static_cast<const TI*>(o_lat), wv, static_cast<TO*>(out))
+    if (o_bf16 && out_bf16) MLA_DECOMP(uint16_t, uint16_t);
+    else if (o_bf16) MLA_DECOMP(uint16_t, float);
+    else if (out_bf16) MLA_DECOMP(float, uint16_t);
+    else MLA_DECOMP(float, float);
+#undef MLA_DECOMP
+    return hipGetLastError();
+  }
+  const unsigned grid = generic_grid(n_tok * H * DV);
+#define MLA_DECOMP_G(TI, TW, TO)                                                                          \
+  hipLaunchKernelGGL((decompress_generic<TI, TW, TO>), dim3(grid), dim3(256), 0, stream, H, DV, KR, n_tok, \
+                     static_cast<const TI*>(o_lat), static_cast<const TW*>(w_uv), static_cast<TO*>(out))
+  if (o_bf16) {
+    if (w_bf16) { if (out_bf16) MLA_DECOMP_G(uint16_t, uint16_t, uint16_t); else MLA_DECOMP_G(uint16_t, uint16_t, float); }
+    else { if (out_bf16) MLA_DECOMP_G(uint16_t, float, uint16_t); else MLA_DECOMP_G(uint16_t, float, float); }
+  } else {
+    if (w_bf16) { if (out_bf16) MLA_DECOMP_G(float, uint16_t, uint16_t); else MLA_DECOMP_G(float, uint16_t, float); }
+    else { if (out_bf16) MLA_DECOMP_G(float, float, uint16_t); else MLA_DECOMP_G(float, float, float); }
+  }
+#undef MLA_DECOMP_G
+  return hipGetLastError();
+}
+
+}  // namespace mla

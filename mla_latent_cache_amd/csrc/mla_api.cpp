@@ -1,0 +1,229 @@
+// C ABI of the MLA latent-cache decode library: argument validation, the
+// split plan, kernel selection and launches.  Declarations and the contract
+// of every entry point are in include/mla.h.
+#include "mla.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+bool dt_ok(mla_dtype d) { return d == MLA_F32 || d == MLA_BF16; }
+
+// Compute units of the current device (cached per device id).
+int device_cus(int* out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return 0;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return -1;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return 0;
+}
+
+mla_status check_decode_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->n_head < 1 || d->kv_rank < 1 || d->d_rope < 0) return MLA_ERR_DIMS;
+  return MLA_OK;
+}
+
+// Automatic split count: enough (request, range, query tile) workgroups for two
+// per compute unit, no range shorter than 8 cache blocks.
+int auto_splits(int n_head, int batch, int t_q, int max_blocks, int cus, bool mfma) {
+  const int n_q = t_q * n_head;
+  const int m_tiles = mfma ? (n_q + mla::kQRowsPerWG - 1) / mla::kQRowsPerWG : n_q;
+  const long base = (long)(batch > 0 ? batch : 1) * m_tiles;
+  long want = (2L * cus + base - 1) / base;
+  const long cap = (max_blocks + 7) / 8;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  if (want > mla::kMaxSplits) want = mla::kMaxSplits;
+  return (int)want;
+}
+
+bool mfma_path(const mla_dims* d, bool bf16) {
+  return bf16 && d->kv_rank == 512 && (d->d_rope == 0 || d->d_rope == 64);
+}
+
+mla_status resolve(const mla_dims* d, int batch, int t_q, int max_blocks, int num_splits, bool bf16,
+                   int* splits) {
+  if (num_splits > 0) {
+    *splits = num_splits;
+    return MLA_OK;
+  }
+  int cus = 0;
+  if (device_cus(&cus) != 0) return MLA_ERR_HIP;
+  *splits = auto_splits(d->n_head, batch, t_q, max_blocks, cus, mfma_path(d, bf16));
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+float mla_default_scale(const mla_dims* dims) {
+  if (!dims || dims->d_nope + dims->d_rope < 1) return NAN;
+  return 1.0f / sqrtf((float)(dims->d_nope + dims->d_rope));
+}
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_DIMS: return "geometry field out of range";
+    case MLA_ERR_SHAPE: return "size argument out of range";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, int64_t n_tok, const void* q_nope, const void* q_pe,
+                        const void* w_uk, mla_dtype in_dt, void* q_abs, mla_dtype out_dt, void* stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (dims->n_head < 1 || dims->d_nope < 1 || dims->kv_rank < 1 || dims->d_rope < 0) return MLA_ERR_DIMS;
+  if (n_tok < 0) return MLA_ERR_SHAPE;
+  if (!dt_ok(in_dt) || !dt_ok(out_dt)) return MLA_ERR_ARG;
+  if (n_tok == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_abs || (dims->d_rope > 0 && !q_pe)) return MLA_ERR_NULL;
+  const hipError_t e = mla::launch_absorb(dims->n_head, dims->d_nope, dims->d_rope, dims->kv_rank, n_tok, q_nope,
+                                          q_pe, w_uk, in_dt == MLA_BF16, q_abs, out_dt == MLA_BF16,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int32_t mla_decode_resolve_splits(const mla_dims* dims, int32_t batch, int32_t t_q, int32_t max_blocks,
+                                  int32_t num_splits) {
+  if (check_decode_dims(dims) != MLA_OK || batch < 0 || t_q < 1 || max_blocks < 1 || num_splits < 0) return 0;
+  int splits = 0;
+  if (resolve(dims, batch, t_q, max_blocks, num_splits, true, &splits) != MLA_OK) return 0;
+  const mla::Plan p = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
+                                       true);
+  return p.splits;
+}
+
+mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t t_q, int32_t max_blocks,
+                                     int32_t block_size, int32_t num_splits, size_t* bytes) {
+  const mla_status st = check_decode_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL;
+  if (batch < 0 || t_q < 1 || max_blocks < 1 || num_splits < 0) return MLA_ERR_SHAPE;
+  if (block_size != 16) return MLA_ERR_UNSUPPORTED;
+  int splits = 0;
+  const mla_status r = resolve(dims, batch, t_q, max_blocks, num_splits, true, &splits);
+  if (r != MLA_OK) return r;
+  // The float32 and bfloat16 paths share one layout; size for the larger.
+  const mla::Plan p1 = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
+                                        true);
+  const mla::Plan p2 = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
+                                        false);
+  *bytes = p1.bytes > p2.bytes ? p1.bytes : p2.bytes;
+  return MLA_OK;
+}
+
+mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_abs,
+                                const void* kv_cache, mla_dtype dt, int64_t num_blocks, int32_t block_size,
+                                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                void* out_lat, mla_dtype out_dt, float* lse, void* workspace,
+                                size_t workspace_bytes, int32_t num_splits, void* stream) {
+  const mla_status st = check_decode_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || t_q < 1 || max_blocks < 1 || num_blocks < 1 || num_splits < 0) return MLA_ERR_SHAPE;
+  if (block_size != 16) return MLA_ERR_UNSUPPORTED;
+  if (!dt_ok(dt) || !dt_ok(out_dt)) return MLA_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return MLA_ERR_ARG;
+  if (!workspace) return MLA_ERR_NULL;
+  if (batch > 0 && (!q_abs || !kv_cache || !block_table || !seq_lens || !out_lat)) return MLA_ERR_NULL;
+  const bool bf16 = dt == MLA_BF16;
+  const bool mfma = mfma_path(dims, bf16);
+  if (!mfma && dims->kv_rank > 1024) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * t_q * dims->n_head > 2147483647LL) return MLA_ERR_SHAPE;
+
+  int splits = 0;
+  const mla_status r = resolve(dims, batch, t_q, max_blocks, num_splits, bf16, &splits);
+  if (r != MLA_OK) return r;
+  const mla::Plan p = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits, bf16);
+  size_t need = 0;
+  const mla_status ws = mla_decode_workspace_size(dims, batch, t_q, max_blocks, block_size, splits, &need);
+  if (ws != MLA_OK) return ws;
+  if (workspace_bytes < need || workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
+
+  mla::DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q_abs;
+  a.kv = kv_cache;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out_lat;
+  a.lse = lse;
+  char* wsb = static_cast<char*>(workspace);
+  a.header = reinterpret_cast<uint32_t*>(wsb);
+  a.status = reinterpret_cast<uint32_t*>(wsb + mla::kHeaderBytes);
+  a.lse_part = reinterpret_cast<float*>(wsb + p.lse_off);
+  a.o_part = reinterpret_cast<float*>(wsb + p.o_off);
+  a.num_blocks = num_blocks;
+  a.batch = batch;
+  a.t_q = t_q;
+  a.n_head = dims->n_head;
+  a.kv_rank = dims->kv_rank;
+  a.d_rope = dims->d_rope;
+  a.max_blocks = max_blocks;
+  a.n_q = t_q * dims->n_head;
+  a.splits = p.splits;
+  a.chunk_blocks = p.chunk_blocks;
+  a.m_tiles = p.m_tiles;
+  a.n_pairs = p.n_pairs;
+  a.n_items = p.n_items;
+  a.scale = scale;
+  a.out_bf16 = out_dt == MLA_BF16;
+  a.direct = p.splits == 1;
+  const hipError_t e = mla::launch_decode(a, mfma, bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_lat, mla_dtype o_dt,
+                            const void* w_uv, mla_dtype w_dt, void* out, mla_dtype out_dt, void* stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (dims->n_head < 1 || dims->d_v < 1 || dims->kv_rank < 1) return MLA_ERR_DIMS;
+  if (n_tok < 0) return MLA_ERR_SHAPE;
+  if (!dt_ok(o_dt) || !dt_ok(w_dt) || !dt_ok(out_dt)) return MLA_ERR_ARG;
+  if (n_tok == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  const hipError_t e = mla::launch_decompress(dims->n_head, dims->d_v, dims->kv_rank, n_tok, o_lat, o_dt == MLA_BF16,
+                                              w_uv, w_dt == MLA_BF16, out, out_dt == MLA_BF16,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_status(const void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags) return MLA_ERR_NULL;
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;
+  uint32_t head[4];
+  if (hipMemcpy(head, workspace, sizeof head, hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
+  if (head[0] != mla::kWorkspaceMagic) return MLA_ERR_WORKSPACE;
+  uint32_t acc = 0;
+  const uint32_t n = head[1];
+  const char* slots = static_cast<const char*>(workspace) + mla::kHeaderBytes;
+  uint32_t buf[1024];
+  for (uint32_t done = 0; done < n;) {
+    const uint32_t k = n - done < 1024u ? n - done : 1024u;
+    if (hipMemcpy(buf, slots + (size_t)done * 4, (size_t)k * 4, hipMemcpyDeviceToHost) != hipSuccess)
+      return MLA_ERR_HIP;
+    for (uint32_t i = 0; i < k; ++i) acc |= buf[i];
+    done += k;
+  }
+  *flags = acc;
+  return MLA_OK;
+}
+
+}  // extern "C"

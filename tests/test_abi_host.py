@@ -1,0 +1,128 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import mla_latent_cache_amd as mla
+from mla_latent_cache_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 8
+    L = mla.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/mla.h but not exported"
+    assert set(names) == set(B.EXPORTS)
+
+
+GLM52 = (64, 192, 64, 256, 512)
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def dims(t=GLM52):
+    return ctypes.byref(B.mla_dims(*t))
+
+
+def decode(**kw):
+    a = dict(dims=dims(), scale=0.0625, batch=2, t_q=1, q=FAKE, kv=FAKE, dt=B.MLA_BF16, num_blocks=10,
+             block_size=16, bt=FAKE, max_blocks=4, sl=FAKE, out=FAKE, out_dt=B.MLA_BF16, lse=None,
+             ws=FAKE, ws_bytes=1 << 30, splits=1, stream=None)
+    a.update(kw)
+    return mla.lib().mla_decode_attention(a["dims"], a["scale"], a["batch"], a["t_q"], a["q"], a["kv"], a["dt"],
+                                          a["num_blocks"], a["block_size"], a["bt"], a["max_blocks"], a["sl"],
+                                          a["out"], a["out_dt"], a["lse"], a["ws"], a["ws_bytes"], a["splits"],
+                                          a["stream"])
+
+
+def test_decode_host_validation():
+    assert decode(dims=None) == B.MLA_ERR_NULL
+    assert decode(dims=dims((0, 192, 64, 256, 512))) == B.MLA_ERR_DIMS
+    assert decode(dims=dims((64, 192, -1, 256, 512))) == B.MLA_ERR_DIMS
+    assert decode(dims=dims((64, 192, 64, 256, 0))) == B.MLA_ERR_DIMS
+    assert decode(batch=-1) == B.MLA_ERR_SHAPE
+    assert decode(t_q=0) == B.MLA_ERR_SHAPE
+    assert decode(max_blocks=0) == B.MLA_ERR_SHAPE
+    assert decode(num_blocks=0) == B.MLA_ERR_SHAPE
+    assert decode(splits=-2) == B.MLA_ERR_SHAPE
+    assert decode(block_size=8) == B.MLA_ERR_UNSUPPORTED
+    assert decode(block_size=32) == B.MLA_ERR_UNSUPPORTED
+    assert decode(dt=7) == B.MLA_ERR_ARG
+    assert decode(out_dt=2) == B.MLA_ERR_ARG
+    assert decode(scale=0.0) == B.MLA_ERR_ARG
+    assert decode(scale=-1.0) == B.MLA_ERR_ARG
+    assert decode(scale=math.nan) == B.MLA_ERR_ARG
+    assert decode(scale=math.inf) == B.MLA_ERR_ARG
+    assert decode(ws=None) == B.MLA_ERR_NULL
+    assert decode(q=None) == B.MLA_ERR_NULL
+    assert decode(kv=None) == B.MLA_ERR_NULL
+    assert decode(bt=None) == B.MLA_ERR_NULL
+    assert decode(sl=None) == B.MLA_ERR_NULL
+    assert decode(out=None) == B.MLA_ERR_NULL
+    assert decode(ws_bytes=16, splits=4) == B.MLA_ERR_WORKSPACE
+
+
+def test_workspace_size_explicit_splits():
+    sz = ctypes.c_size_t()
+    L = mla.lib()
+    assert L.mla_decode_workspace_size(dims(), 32, 1, 256, 16, 1, ctypes.byref(sz)) == B.MLA_OK
+    one = sz.value
+    assert one >= 256 and one % 256 == 0
+    assert L.mla_decode_workspace_size(dims(), 32, 1, 256, 16, 8, ctypes.byref(sz)) == B.MLA_OK
+    eight = sz.value
+    # eight splits need per-split (o, lse) partials: 32 * 8 * 64 * (512 + 1) float32 at least
+    assert eight >= 32 * 8 * 64 * 513 * 4 and eight > one
+    assert L.mla_decode_workspace_size(dims(), 32, 1, 256, 8, 8, ctypes.byref(sz)) == B.MLA_ERR_UNSUPPORTED
+    assert L.mla_decode_workspace_size(dims(), 32, 0, 256, 16, 8, ctypes.byref(sz)) == B.MLA_ERR_SHAPE
+    assert L.mla_decode_workspace_size(dims(), 32, 1, 256, 16, 8, None) == B.MLA_ERR_NULL
+    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 8) == 8
+    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 7) == 7   # 37 blocks per range, 7 ranges
+    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 500) == 256
+    assert L.mla_decode_resolve_splits(dims(), 32, 0, 256, 8) == 0
+
+
+def test_absorb_and_decompress_host_validation():
+    L = mla.lib()
+    assert L.mla_absorb_q(None, 4, FAKE, FAKE, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_NULL
+    assert L.mla_absorb_q(dims((64, 0, 64, 256, 512)), 4, FAKE, FAKE, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_DIMS
+    assert L.mla_absorb_q(dims(), -1, FAKE, FAKE, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_SHAPE
+    assert L.mla_absorb_q(dims(), 4, FAKE, FAKE, FAKE, 3, FAKE, 1, None) == B.MLA_ERR_ARG
+    assert L.mla_absorb_q(dims(), 4, FAKE, None, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_NULL  # rope needed
+    assert L.mla_absorb_q(dims(), 0, None, None, None, 1, None, 1, None) == B.MLA_OK          # empty: no-op
+    assert L.mla_decompress_v(None, 4, FAKE, 1, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_NULL
+    assert L.mla_decompress_v(dims((64, 192, 64, 0, 512)), 4, FAKE, 1, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_DIMS
+    assert L.mla_decompress_v(dims(), -3, FAKE, 1, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_SHAPE
+    assert L.mla_decompress_v(dims(), 4, FAKE, 1, FAKE, 9, FAKE, 1, None) == B.MLA_ERR_ARG
+    assert L.mla_decompress_v(dims(), 4, None, 1, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_NULL
+    assert L.mla_decode_status(None, None, None) == B.MLA_ERR_NULL
+
+
+def test_default_scale_and_strings():
+    assert mla.mla_default_scale(GLM52) == pytest.approx(1 / 16, abs=1e-9)
+    assert mla.mla_default_scale((64, 256, 0, 256, 512)) == pytest.approx(1 / 16, abs=1e-9)
+    assert mla.mla_default_scale((4, 16, 8, 16, 32)) == pytest.approx(1 / math.sqrt(24), rel=1e-7)
+    assert math.isnan(mla.lib().mla_default_scale(None))
+    for code in range(8):
+        assert len(mla.mla_status_string(code)) > 0
+    assert mla.mla_status_string(99) == "unknown status"
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 64, 192, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mla.mla_absorb_q(GLM52, x, torch.zeros(4, 64, 64, dtype=torch.bfloat16),
+                         torch.zeros(64, 192, 512, dtype=torch.bfloat16),
+                         torch.zeros(4, 64, 576, dtype=torch.bfloat16))

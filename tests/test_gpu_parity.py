@@ -1,0 +1,232 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Small cases compare every output element; the full-size workloads run in
+the benchmark's launch configuration (automatic split count) and compare a
+seeded sample of (request, query, head) outputs that the oracle computes one
+by one.  Property tests cover split invariance, determinism, block relabelling,
+the value slice, the causal mask, empty requests and device-side data errors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import mla_latent_cache_amd as mla
+import oracle
+from gpu_util import (DeviceCase, assert_close, assert_lse_close, dims_tuple, flat_index, oracle_dims,
+                      oracle_q_abs, paged, run, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on a GPU machine only
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def spec_small(name, base, **kw):
+    return mi.with_spec(mi.SPECS[base], name=name, **kw)
+
+
+def full_compare(case, res, sel=None, naive_items=0):
+    """Compare absorb, decode and decompress outputs of `res` with the oracle."""
+    s = case.spec
+    d = oracle_dims(s)
+    if not s.q_given:
+        qa = oracle_q_abs(case)
+        assert_close(to_host(res["q_abs"]).reshape(qa.shape), qa, s.dtype, "q_abs")
+    o_ref, lse_ref, bad = oracle.decode(d, s.t_q, oracle_q_abs(case), paged(case), case.scale, sel=sel)
+    assert bad == 0
+    idx = flat_index(s, sel) if sel is not None else slice(None)
+    o_gpu = to_host(res["o_lat"]).reshape(-1, s.kv_rank)[idx]
+    lse_gpu = to_host(res["lse"]).reshape(-1)[idx]
+    assert_close(o_gpu, o_ref, s.dtype, "o_lat")
+    assert_lse_close(lse_gpu, lse_ref, s.dtype, "lse")
+    if not s.q_given:
+        out_ref, o2, lse2, _ = oracle.attend_absorbed(d, s.t_q, case.q_nope, case.q_pe, case.w_uk, case.w_uv,
+                                                      paged(case), case.scale, sel=sel)
+        out_gpu = to_host(res["out"]).reshape(-1, s.d_v)[idx]
+        assert_close(out_gpu, out_ref, s.dtype, "out")
+        if naive_items:
+            sel_n = sel[:naive_items] if sel is not None else mi.sample_items(7, s.batch, s.t_q, s.n_head,
+                                                                              naive_items)
+            out_n, _, _ = oracle.attend_naive(d, s.t_q, case.q_nope, case.q_pe, case.w_uk, case.w_uv,
+                                              paged(case), case.scale, sel=sel_n)
+            assert_close(to_host(res["out"]).reshape(-1, s.d_v)[flat_index(s, sel_n)], out_n, s.dtype,
+                         "out vs naive form")
+
+
+# --------------------------------------------------------------------------
+# Small cases, every element
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3])
+def test_tiny_f32_full_pipeline(num_splits):
+    case = mi.make_case(mi.SPECS["tiny_f32"])
+    res = run(DeviceCase(case), num_splits=num_splits)
+    assert res["status"] == 0
+    full_compare(case, res, naive_items=8)
+
+
+SMALL = {
+    "glm52_small": dict(base="glm52_decode", batch=5, fixed_lens=(1, 17, 100, 300, 64), max_blocks=20),
+    "glm52_causal_small": dict(base="glm52_causal_tq4", batch=3, fixed_lens=(4, 35, 130), max_blocks=9),
+    "nope_small": dict(base="nope_long", batch=3, fixed_lens=(33, 2, 257), max_blocks=17),
+    "dsv3_small": dict(base="dsv3_ragged", batch=4, fixed_lens=(0, 50, 700, 16), max_blocks=44,
+                       lengths="fixed", zero_requests=(0,)),
+}
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 0])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_bf16_every_element(name, num_splits):
+    kw = dict(SMALL[name])
+    spec = spec_small(name, kw.pop("base"), **kw)
+    case = mi.make_case(spec)
+    res = run(DeviceCase(case), num_splits=num_splits)
+    assert res["status"] == 0
+    full_compare(case, res, naive_items=0 if spec.q_given else 4)
+
+
+def test_boundary_lengths_and_empty_requests():
+    lens = (0, 1, 15, 16, 17, 31, 32, 33, 0, 63, 64, 65)
+    spec = spec_small("glm52_edges", "glm52_decode", batch=len(lens), fixed_lens=lens, max_blocks=6)
+    case = mi.make_case(spec)
+    for num_splits in (1, 2, 4):
+        res = run(DeviceCase(case), num_splits=num_splits, out_dtype=torch.float32)
+        assert res["status"] == 0
+        o = to_host(res["o_lat"])
+        lse = to_host(res["lse"])
+        out = to_host(res["out"]).reshape(len(lens), 1, spec.n_head, spec.d_v)
+        for b in (0, 8):  # empty requests: exact zeros and -inf
+            assert np.all(o[b] == 0.0) and not np.signbit(o[b]).any()
+            assert np.all(np.isneginf(lse[b]))
+            assert np.all(out[b] == 0.0)
+        full_compare(case, res)
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads, launch configuration of the benchmark, sampled outputs
+# --------------------------------------------------------------------------
+FULL = {
+    "glm52_decode": dict(n=96, naive=2),
+    "dsv3_ragged": dict(n=160, naive=0),
+    "glm52_causal_tq4": dict(n=96, naive=2),
+    "nope_long": dict(n=64, naive=0),
+    "nope_wide": dict(n=96, naive=2),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled(name):
+    spec = mi.SPECS[name]
+    case = mi.make_case(spec)
+    res = run(DeviceCase(case), num_splits=0)
+    assert res["status"] == 0
+    must = []
+    if name == "dsv3_ragged":
+        longest = int(np.argmax(case.seq_lens))
+        must = [(0, 0, 0), (0, 0, 127), (63, 0, 5), (longest, 0, 0), (longest, 0, 127)]
+    if spec.t_q > 1:
+        must = [(0, i, h) for i in range(spec.t_q) for h in (0, 63)]
+    sel = mi.sample_items(spec.seed, spec.batch, spec.t_q, spec.n_head, FULL[name]["n"], must=must)
+    full_compare(case, res, sel=sel, naive_items=FULL[name]["naive"])
+    if name == "dsv3_ragged":  # every head of the two empty requests
+        o = to_host(res["o_lat"])
+        lse = to_host(res["lse"])
+        for b in (0, 63):
+            assert np.all(o[b] == 0.0) and np.all(np.isneginf(lse[b]))
+    assert np.isfinite(to_host(res["o_lat"])[case.seq_lens > 0]).all()
+
+
+# --------------------------------------------------------------------------
+# Properties
+# --------------------------------------------------------------------------
+def mid_case(**kw):
+    spec = spec_small("glm52_mid", "glm52_decode", batch=4, fixed_lens=(700, 1000, 33, 257), max_blocks=64, **kw)
+    return mi.make_case(spec)
+
+
+def test_split_invariance_and_determinism():
+    case = mid_case()
+    dc = DeviceCase(case)
+    outs = {}
+    for k in (1, 2, 7, 0, 64):
+        r1 = run(dc, num_splits=k, out_dtype=torch.float32)
+        r2 = run(dc, num_splits=k, out_dtype=torch.float32)
+        a, b = to_host(r1["o_lat"]), to_host(r2["o_lat"])
+        assert np.array_equal(a, b), f"num_splits={k}: two runs differ"
+        assert np.array_equal(to_host(r1["lse"]), to_host(r2["lse"]))
+        outs[k] = (a, to_host(r1["lse"]))
+    ref, lref = outs[1]
+    scale = np.abs(ref).max()
+    for k, (o, l) in outs.items():
+        # different ranges change where bf16 probabilities are rounded and the f32 sum order
+        assert np.abs(o - ref).max() <= 2e-3 * scale, k
+        assert np.abs(l - lref).max() <= 1e-4 * max(1.0, np.abs(lref).max()), k
+
+
+def test_relabelled_blocks_bit_identical():
+    case = mid_case()
+    case2 = mi.make_case(case.spec, relabel_seed=4242)
+    assert not np.array_equal(case.block_table, case2.block_table)
+    for k in (1, 3):
+        r1 = run(DeviceCase(case), num_splits=k)
+        r2 = run(DeviceCase(case2), num_splits=k)
+        for key in ("o_lat", "lse", "out"):
+            assert torch.equal(r1[key], r2[key]), (k, key)
+
+
+def test_value_is_leading_kv_rank_slice():
+    spec = spec_small("dsv3_vslice", "dsv3_ragged", batch=3, fixed_lens=(40, 300, 17), max_blocks=19,
+                      lengths="fixed", zero_requests=())
+    case = mi.make_case(spec)
+    case.q_abs[..., 512:] = 0  # rope part of the queries zero: k_pe adds exact zeros to every score
+    r1 = run(DeviceCase(case), num_splits=2)
+    kv2 = case.kv.copy()
+    live = np.isfinite(mi.widen(kv2))
+    big = mi.to_bf16_bits(np.full(kv2[..., 512:].shape, 3.0e4, np.float32))
+    kv2[..., 512:] = np.where(live[..., 512:], big, kv2[..., 512:])
+    case2 = mi.Case(case.spec, case.seq_lens, case.block_table, kv2, None, None, None, None, case.q_abs)
+    r2 = run(DeviceCase(case2), num_splits=2)
+    assert torch.equal(r1["o_lat"], r2["o_lat"])
+    assert torch.equal(r1["lse"], r2["lse"])
+
+
+def test_causal_mask_probe():
+    spec = spec_small("causal_probe", "glm52_causal_tq4", batch=2, fixed_lens=(37, 200), max_blocks=13)
+    case = mi.make_case(spec)
+    r1 = run(DeviceCase(case), num_splits=1)
+    kv2 = case.kv.copy()
+    for b, L in enumerate(case.seq_lens):
+        j = int(L) - 1  # the last row: visible only to the last query of request b
+        kv2[case.block_table[b, j // 16], j % 16, :] = mi.to_bf16_bits(np.full(spec.D, 2.5, np.float32))
+    case2 = mi.Case(case.spec, case.seq_lens, case.block_table, kv2, case.q_nope, case.q_pe, case.w_uk,
+                    case.w_uv, None)
+    r2 = run(DeviceCase(case2), num_splits=1)
+    o1, o2 = r1["o_lat"], r2["o_lat"]
+    assert torch.equal(o1[:, :3], o2[:, :3]), "queries 0..t_q-2 must not see the last row"
+    assert not torch.equal(o1[:, 3], o2[:, 3])
+
+
+def test_data_errors_flag_and_poison_only_their_request():
+    spec = spec_small("errs", "glm52_causal_tq4", batch=6, fixed_lens=(40, 40, 40, 40, 40, 40), max_blocks=4)
+    case = mi.make_case(spec)
+    dc = DeviceCase(case)
+    clean = run(dc, num_splits=2, out_dtype=torch.float32)
+    assert clean["status"] == 0
+    lens = case.seq_lens.copy()
+    lens[0] = -3                       # negative length
+    lens[1] = 4 * 16 + 1               # beyond the block-table row
+    lens[2] = 2                        # fewer rows than queries
+    bt = case.block_table.copy()
+    bt[3, 1] = case.num_blocks + 5     # block id out of range
+    bt[4, 2] = -7                      # negative block id inside the request
+    res = run(dc, num_splits=2, out_dtype=torch.float32, seq_lens=torch.from_numpy(lens).cuda(),
+              block_table=torch.from_numpy(bt).cuda())
+    assert res["status"] == (mla.MLA_DATA_NEG_LEN | mla.MLA_DATA_LEN_OVER_TABLE | mla.MLA_DATA_LEN_BELOW_TQ
+                             | mla.MLA_DATA_BAD_BLOCK)
+    o = to_host(res["o_lat"])
+    for b in range(5):
+        assert np.isnan(o[b]).all(), b
+        assert np.isnan(to_host(res["lse"])[b]).all(), b
+    assert torch.equal(res["o_lat"][5], clean["o_lat"][5])
+    again = run(dc, num_splits=2, out_dtype=torch.float32)
+    assert again["status"] == 0 and torch.equal(again["o_lat"], clean["o_lat"])
