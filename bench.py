@@ -1,0 +1,269 @@
+"""Benchmark of the MLA latent-cache decode hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input,
+with every input already resident in HBM:
+    mla_absorb_q -> mla_decode_attention (split-KV kernel + LSE merge) -> mla_decompress_v
+Default workload: GLM-5.2 geometry decode (64 heads, d_nope 192, d_rope 64,
+d_v 256, kv_rank 512; 32 requests x 4096 cached rows; 16-row blocks; bf16).
+
+Consecutive steps cycle through --copies independent copies of every input
+(cache, block table, queries, weights), so the 256 MB Infinity Cache cannot
+serve a step from the previous one.  HIP events on the launch stream time
+each stage live inside the timed region.  The CPU baseline runs the oracle
+(absorbed form: absorb, two-pass attention, decompress) over the same
+workload on the host cores.
+
+Prints one JSON line.  Throughput `value` is algorithmic decode-path bytes
+per second (GB/s): KV rows read once, queries, weights, outputs, block table
+and lengths; the split partials are not counted.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode GB/s & TFLOP/s (% HBM/MFMA roofline); tokens·heads/s vs CPU oracle"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def work_figures(spec, seq_lens):
+    """Algorithmic bytes / flops / tokens*heads of one step, per stage."""
+    import numpy as np
+    L = np.asarray(seq_lens, dtype=np.int64)
+    B, T, H, D, R = spec.batch, spec.t_q, spec.n_head, spec.D, spec.kv_rank
+    e = 4 if spec.dtype == "f32" else 2
+    n_tok = B * T
+    vis = 0
+    for l in L:
+        if l > 0:
+            vis += sum(int(l) - T + i + 1 for i in range(T))
+    kv_rows = int(L[L > 0].sum())
+    blocks = int(((L[L > 0] + 15) // 16).sum())
+    f = {}
+    f["absorb_bytes"] = 0 if spec.q_given else (n_tok * H * (spec.d_nope + spec.d_rope) * e
+                                                + H * spec.d_nope * R * e + n_tok * H * D * e)
+    f["absorb_flops"] = 0 if spec.q_given else 2 * n_tok * H * spec.d_nope * R
+    f["decode_bytes"] = (kv_rows * D * e + n_tok * H * D * e + n_tok * H * R * e + n_tok * H * 4
+                         + blocks * 4 + B * 4)
+    f["decode_flops"] = vis * H * 2 * (D + R)
+    f["decompress_bytes"] = 0 if spec.q_given else (n_tok * H * R * e + H * spec.d_v * R * e
+                                                    + n_tok * H * spec.d_v * e)
+    f["decompress_flops"] = 0 if spec.q_given else 2 * n_tok * H * spec.d_v * R
+    f["kv_bytes"] = kv_rows * D * e
+    f["tokens_heads"] = vis * H
+    f["bytes"] = f["absorb_bytes"] + f["decode_bytes"] + f["decompress_bytes"]
+    f["flops"] = f["absorb_flops"] + f["decode_flops"] + f["decompress_flops"]
+    return f
+
+
+def cpu_baseline(spec, case, figs, max_items: int):
+    """The oracle (absorbed form) timed on the host cores over the workload, or
+    over a seeded sample of max_items (request, query, head) items."""
+    import numpy as np
+    import mla_inputs as mi
+    import oracle
+
+    n_all = spec.batch * spec.t_q * spec.n_head
+    d = oracle.Dims(spec.n_head, spec.d_nope, spec.d_rope, spec.d_v, spec.kv_rank)
+    paged = oracle.Paged(case.kv, case.block_table, case.seq_lens)
+    sel = None if n_all <= max_items else mi.sample_items(spec.seed + 1, spec.batch, spec.t_q, spec.n_head,
+                                                          max_items)
+    n = n_all if sel is None else len(sel)
+    t0 = time.perf_counter()
+    if spec.q_given:
+        oracle.decode(d, spec.t_q, case.q_abs, paged, case.scale, sel=sel)
+    else:
+        oracle.attend_absorbed(d, spec.t_q, case.q_nope, case.q_pe, case.w_uk, case.w_uv, paged, case.scale,
+                               sel=sel)
+    dt = time.perf_counter() - t0
+    frac = n / n_all  # items are independent: the sample does this share of the step's work
+    gbs = figs["bytes"] * frac / dt / 1e9
+    return {
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": ("whole workload" if sel is None else f"{n} of {n_all} (request, query, head) items, seeded")
+                  + f", absorbed form in float64, {dt:.2f} s wall",
+        "tokens_heads_per_s": round(figs["tokens_heads"] * frac / dt, 1),
+        "seconds": round(dt, 3),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="glm52_decode")
+    ap.add_argument("--copies", type=int, default=4, help="input copies cycled across steps")
+    ap.add_argument("--num-splits", type=int, default=0, help="KV splits per request (0 = automatic)")
+    ap.add_argument("--cpu-items", type=int, default=4096, help="oracle items for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs the "
+              "decode path on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_latent_cache_amd as mla
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    mla.lib()  # fails loudly when the HIP library is missing
+    torch.cuda.set_device(0)
+    spec = mi.SPECS[args.workload]
+    log(f"workload {spec.name}: generating inputs")
+    case = mi.make_case(spec)
+    figs = work_figures(spec, case.seq_lens)
+    dims = (spec.n_head, spec.d_nope, spec.d_rope, spec.d_v, spec.kv_rank)
+    B, T, H, D, R = spec.batch, spec.t_q, spec.n_head, spec.D, spec.kv_rank
+    sdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    copies = []
+    for k in range(max(1, args.copies)):
+        c = {"kv": dev(case.kv), "bt": torch.from_numpy(case.block_table).cuda(),
+             "sl": torch.from_numpy(case.seq_lens).cuda()}
+        if spec.q_given:
+            c["q_abs"] = dev(case.q_abs)
+        else:
+            c.update(q_nope=dev(case.q_nope), q_pe=dev(case.q_pe) if spec.d_rope else None,
+                     w_uk=dev(case.w_uk), w_uv=dev(case.w_uv),
+                     q_abs=torch.empty(B, T, H, D, dtype=sdt, device="cuda"))
+        c["out_lat"] = torch.empty(B, T, H, R, dtype=sdt, device="cuda")
+        c["lse"] = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
+        if not spec.q_given:
+            c["out"] = torch.empty(B * T, H, spec.d_v, dtype=sdt, device="cuda")
+        copies.append(c)
+    splits = mla.mla_decode_resolve_splits(dims, B, T, spec.max_blocks, args.num_splits)
+    ws = torch.empty(mla.mla_decode_workspace_size(dims, B, T, spec.max_blocks, 16, args.num_splits),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(c, ev=None):
+        if not spec.q_given:
+            mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode_attention(dims, case.scale, c["q_abs"], c["kv"], c["bt"], c["sl"], c["out_lat"], c["lse"],
+                                 ws, args.num_splits, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if not spec.q_given:
+            mla.mla_decompress_v(dims, c["out_lat"], c["w_uv"], c["out"], stream)
+
+    log(f"warmup {args.warmup} steps ({splits} splits per request, {len(copies)} input copies)")
+    for k in range(args.warmup):
+        step(copies[k % len(copies)])
+    torch.cuda.synchronize()
+    status = mla.mla_decode_status(ws)
+    if status:
+        log(f"device data-error flags {status:#x}")
+        return 1
+
+    # Timed region: the whole step, and the decode call alone on the same stream.
+    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(args.steps):
+        step(copies[k % len(copies)], ev_dec[k])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    dec_ms = sorted(a.elapsed_time(b) for a, b in ev_dec)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    log(f"{ms_step * 1e3:.1f} us/step; decode call avg {dec_avg * 1e3:.1f} us (min {dec_ms[0] * 1e3:.1f})")
+
+    # Stage split (separate, untimed-for-value pass): absorb and decompress alone.
+    stage = {}
+    if not spec.q_given:
+        for name in ("absorb", "decompress"):
+            es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for k, (a, b) in enumerate(es):
+                c = copies[k % len(copies)]
+                a.record(stream)
+                if name == "absorb":
+                    mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
+                else:
+                    mla.mla_decompress_v(dims, c["out_lat"], c["w_uv"], c["out"], stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            stage[name] = sum(a.elapsed_time(b) for a, b in es) / len(es)
+    stage["decode"] = dec_avg
+
+    value = figs["bytes"] / (ms_step * 1e-3) / 1e9
+    dec_gbs = figs["decode_bytes"] / (dec_avg * 1e-3) / 1e9
+    dec_tflops = figs["decode_flops"] / (dec_avg * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded SplitMix64 normals; RMS-normalised latent rows; shuffled block tables)",
+        "config": {
+            "workload": f"{spec.name}: {H} heads, d_nope {spec.d_nope}, d_rope {spec.d_rope}, d_v {spec.d_v}, "
+                        f"kv_rank {R}, batch {B} x t_q {T}, cache rows per request "
+                        f"{'ragged' if spec.lengths == 'ragged' else int(case.seq_lens[0])}, block 16",
+            "batch": B, "t_q": T, "seq_lens_total": int(np.maximum(case.seq_lens, 0).sum()),
+            "splits_per_request": splits, "input_copies": len(copies),
+        },
+        "tflops": round(figs["flops"] / (ms_step * 1e-3) / 1e12, 3),
+        "tokens_heads_per_s": round(figs["tokens_heads"] / (ms_step * 1e-3), 1),
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "roofline": {
+            "kernel": "decode call: decode_split_mfma + decode_merge",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": figs["decode_bytes"],
+            "avg_launch_us": round(dec_avg * 1e3, 2),
+            "mfma_tflops": round(dec_tflops, 2),
+            "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on host cores")
+        result["cpu_baseline"] = cpu_baseline(spec, case, figs, args.cpu_items)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -8,18 +8,21 @@
 // lse = log sum_j exp(s_j).
 //
 // Schedule.  The rows of a request are cut into `splits` ranges of whole cache
-// blocks.  One workgroup handles one (request, range, tile of 64 query rows);
-// it walks its range 32 rows (two 16-row cache blocks) at a time:
-//   * the two blocks go HBM -> LDS directly (buffer_load ... lds), one buffer
-//     resource per block, so rows past the request's end read as zeros and no
-//     address outside a real block is ever formed;
-//   * each of the 4 waves owns 16 query rows and computes S^T = K Q^T with
-//     16x16x32 bf16 MFMA (K rows from LDS as the A operand, its absorbed
-//     queries resident in VGPRs as the B operand);
-//   * the running max / sum update happens in registers; P^T is then already
-//     in the B-operand layout of O^T = V^T P^T, and V^T comes from the same
-//     LDS tile through the transposing ds_read_b64_tr_b16;
-//   * the next tile's loads are in flight while the current one is consumed.
+// blocks.  One workgroup handles one (request, range, tile of 64 query rows)
+// and walks its range 32 rows (two 16-row cache blocks) at a time:
+//   * blocks go HBM -> LDS directly (buffer_load ... lds), one buffer resource
+//     per block, so rows past the request's end read as zeros and no address
+//     outside a real block is formed; a ring of three tile buffers keeps two
+//     tiles in flight while one is consumed;
+//   * wave (qh, dh) owns query rows [32 qh, 32 qh + 32) of the tile and half
+//     dh of the row width: it computes the partial S^T = K Q^T over its half
+//     of D with 16x16x32 bf16 MFMA (every K read from LDS feeds two MFMAs),
+//     trades partials with its partner wave through LDS, and both partners
+//     then hold the same full scores and run the same online softmax;
+//   * P^T is already in the B-operand layout of O^T = V^T P^T; wave (qh, dh)
+//     accumulates output columns [256 dh, 256 dh + 256) for its 32 query rows,
+//     reading V^T from the same LDS tile with the transposing ds_read_b64_tr_b16
+//     (again one read per two MFMAs).
 // With one range per request the workgroup writes the final output and LSE;
 // otherwise it writes (o, lse) partials and decode_merge combines them:
 //   M = max_s lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
@@ -66,6 +69,27 @@ __device__ __forceinline__ void write_header(const DecodeArgs& a) {
   }
 }
 
+// s_waitcnt with vmcnt <= N and no constraint on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier that keeps vector-memory loads in flight: it waits only
+// for this wave's LDS accesses, unlike __syncthreads(), whose release fence
+// also waits for every outstanding global load.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kIdWindow = 512;  // cache-block ids of a range staged in LDS at a time
+constexpr float kSlack = 8.f;   // log2 headroom before the softmax reference moves
+
 // ---------------------------------------------------------------------------
 // MFMA split kernel: bf16 queries and cache, kv_rank 512, rope width D_ROPE.
 // ---------------------------------------------------------------------------
@@ -79,23 +103,30 @@ struct Tile {
   static constexpr int BLK_IMG = (BLK_POS + 63) / 64 * 64; // whole wave-loads per block
   static constexpr int BLK_LOADS = BLK_IMG / 64;
   static constexpr int IMG = 2 * BLK_IMG;                  // one 32-row tile
-  static constexpr int KSTEPS = D / 32;
-  static constexpr int CT = KV / 16;
+  static constexpr int KSTEPS = D / 32;                    // 32-wide k-steps of S
+  static constexpr int KH = KSTEPS / 2;                    // k-steps per half of D
+  static constexpr int CTH = KV / 32;                      // 16-column output tiles per half
   static_assert((STRIDE * 4) % 16 == 8, "row stride must be 8 * odd dwords");
+  static_assert(KSTEPS % 2 == 0, "D must split into two halves of whole k-steps");
 };
 
 template <int D_ROPE>
 __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) {
   using T = Tile<D_ROPE>;
-  constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KSTEPS = T::KSTEPS, CT = T::CT;
+  constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KH = T::KH, CTH = T::CTH;
   __shared__ __attribute__((aligned(16))) u32x4 lds0[T::IMG];
   __shared__ __attribute__((aligned(16))) u32x4 lds1[T::IMG];
+  __shared__ __attribute__((aligned(16))) u32x4 lds2[T::IMG];
+  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];  // S partials: [wave][rt * 2 + n][lane]
+  __shared__ int32_t id_lds[kIdWindow];
 
   write_header(a);
   int b, s, mt, item;
   if (!decode_item(a, b, s, mt, item)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int qh = w >> 1, dh = w & 1;
   const int l16 = lane & 15, g = lane >> 4;
 
   const int64_t L = a.seq_lens[b];
@@ -105,39 +136,59 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
   if (flags || r_end > L) r_end = flags ? r_begin : L;
   const int n_tiles = r_end > r_begin ? (int)((r_end - r_begin + 31) / 32) : 0;
 
-  // This lane's query row (B/C-operand column) and its causal horizon.
-  const int q_lane = mt * kQRowsPerWG + w * 16 + l16;
-  const bool q_ok = q_lane < a.n_q;
-  const int64_t horizon = L - a.t_q + (q_ok ? q_lane / a.n_head : 0) + 1;
-
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + q_lane) * D + 8 * g;
+  // The lane's query rows in the wave's two 16-row tiles n = 0, 1, and how
+  // many rows of the range each of them sees (range end and causal horizon).
+  int q_row[2], vis_lim[2];
+  bool q_ok[2];
 #pragma unroll
-    for (int t = 0; t < KSTEPS; ++t)
-      qf[t] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 32 * t) : zero_bf16x8();
+  for (int n = 0; n < 2; ++n) {
+    q_row[n] = mt * kQRowsPerWG + 32 * qh + 16 * n + l16;
+    q_ok[n] = q_row[n] < a.n_q;
+    const int64_t horizon = L - a.t_q + (q_ok[n] ? q_row[n] / a.n_head : 0) + 1;
+    const int64_t vis_end = horizon < r_end ? horizon : r_end;
+    vis_lim[n] = !q_ok[n] || vis_end <= r_begin ? 0 : (int)(vis_end - r_begin);
   }
+
+  // B operand of S^T: absorbed queries of both tiles over this wave's half of D.
+  bf16x8 qf[2][KH];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + q_row[n]) * D +
+                         32 * KH * dh + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KH; ++kk)
+      qf[n][kk] = q_ok[n] ? *reinterpret_cast<const bf16x8*>(qp + 32 * kk) : zero_bf16x8();
+  }
+  wait_vmcnt<0>();  // queries resident before the tile loop (keeps its waits exact)
   const float sl2 = a.scale * kLog2e;
 
-  f32x4 acc[CT];
+  f32x4 acc[CTH][2];
 #pragma unroll
-  for (int c = 0; c < CT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m2 = -INFINITY, lsum = 0.f;
+  for (int c = 0; c < CTH; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
 
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
 
-  // Block ids of the tile starting at row r0 (scalar loads; -1 past the range end).
-  auto tile_ids = [&](int64_t r0, int32_t* ids) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int64_t row0 = r0 + hb * 16;
-      ids[hb] = -1;
-      if (row0 < r_end) ids[hb] = bt_row[__builtin_amdgcn_readfirstlane((int)(row0 >> 4))];
+  // Block ids of the range are staged in LDS, kIdWindow at a time, so the loop
+  // reads them without a vector-memory wait (which would also wait for the
+  // tiles in flight).  Tile t uses range-relative slots 2t and 2t + 1.
+  const int slot0 = s * a.chunk_blocks;
+  const int nslots = (int)((r_end - r_begin + 15) / 16);
+  auto load_ids = [&](int win0) {
+    for (int i = tid; i < kIdWindow; i += 256) {
+      const int rel = win0 + i;
+      id_lds[i] = rel < nslots ? bt_row[slot0 + rel] : -1;
     }
   };
+  auto tile_ids = [&](int t, int win0, int32_t* ids) {
+    ids[0] = __builtin_amdgcn_readfirstlane(id_lds[2 * t - win0]);
+    ids[1] = __builtin_amdgcn_readfirstlane(id_lds[2 * t + 1 - win0]);
+  };
 
-  // Per-lane byte offsets of this wave's share of one block image (identical for every block).
+  // This wave's share of the 64-chunk wave-loads of one block image, as byte
+  // offsets into the block (the same for every block).  Rows 8..15 of a block
+  // swap the two 16-byte chunks of each 32-byte pair (bank spreading).
   constexpr int WAVE_LOADS = (T::BLK_LOADS + 3) / 4;
   uint32_t voffs[WAVE_LOADS];
 #pragma unroll
@@ -147,44 +198,50 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
     const int cp = pos - rl * STRIDE;
     voffs[u] = (rl < 16 && cp < CH) ? (uint32_t)(rl * D + ((cp ^ ((rl >> 3) & 1)) * 8)) * 2u : 0x7ffffff0u;
   }
-
-  // Issue the loads of the tile starting at row r0 (block ids `ids`) into buffer `dst`.
-  auto issue = [&](int64_t r0, const int32_t* ids, u32x4* dst) {
+  int c_w = 0;  // this wave's buffer loads per tile (for the vmcnt waits)
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+  for (int u = 0; u < WAVE_LOADS; ++u) c_w += (w + 4 * u < T::BLK_LOADS) ? 2 : 0;
+
+  // Issue the loads of block hb (0 or 1) of tile t (block ids `ids`) into buffer `dst`.
+  auto issue_block = [&](int t, int hb, const int32_t* ids, u32x4* dst) {
+    const int64_t r0 = r_begin + (int64_t)t * 32;
+    {
       const int64_t left = r_end - (r0 + hb * 16);
       const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
       const int32_t id = ids[hb];
       const bool ok = id >= 0 && (int64_t)id < a.num_blocks;
       if (nvalid > 0 && !ok) flags |= kBadBlock;
       const uint16_t* base = ok ? kv + (int64_t)id * 16 * D : kv;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, ok ? (uint32_t)(nvalid * D * 2) : 0u);
+      const i32x4 rs = raw_rsrc(base, ok ? (uint32_t)(nvalid * D * 2) : 0u);
+      const uint32_t lbase = lds_addr(dst + hb * T::BLK_IMG);
 #pragma unroll
-      for (int u = 0; u < WAVE_LOADS; ++u)
-        if (w + 4 * u < T::BLK_LOADS) buffer_load_lds16(rs, dst + hb * T::BLK_IMG + (w + 4 * u) * 64, voffs[u]);
+      for (int u = 0; u < WAVE_LOADS; ++u) {
+        if (w + 4 * u < T::BLK_LOADS) dma16(rs, lbase + (uint32_t)((w + 4 * u) * 64 * 16), voffs[u]);
+      }
     }
   };
 
   // Per-lane LDS offsets.  Tile row r, chunk c lives at chunk slot
   // (r / 16) * BLK_IMG + (r % 16) * STRIDE + (c ^ sw), sw = ((r % 16) >> 3) & 1;
-  // since sw only flips bit 0, chunk 4t + g maps to 4t + (g ^ sw) and chunk
-  // 2ct + x to 2ct + (x ^ sw): every address below is lane base + constant.
-  const int sw_k = (l16 >> 3) & 1;                       // rows l16 and 16 + l16
-  const int k_base = l16 * STRIDE + (g ^ sw_k);          // chunk slot of (row l16, chunk g)
-  const int rr = 4 * g + (l16 >> 2);                     // V rows rr and 16 + rr
+  // sw only flips bit 0, so every address below is a lane base plus a constant.
+  // K (A operand of S^T) for k-step kk of half dh: row l16 (+16 rt), chunk 4 (KH dh + kk) + g.
+  const int sw_k = (l16 >> 3) & 1;
+  const int k_base = l16 * STRIDE + ((4 * KH * dh + g) ^ sw_k);
+  // V^T (A operand of O^T) for column tile ct of half dh: rows rr and 16 + rr,
+  // columns 256 dh + 16 ct + 4 (l16 % 4) .. + 3.
+  const int rr = 4 * g + (l16 >> 2);
   const int sw_v = (rr >> 3) & 1;
-  const int v_base = (rr * STRIDE + (((l16 & 3) >> 1) ^ sw_v)) * 16 + (l16 & 1) * 8;  // bytes
+  const int v_base = (rr * STRIDE + ((32 * dh + ((l16 & 3) >> 1)) ^ sw_v)) * 16 + (l16 & 1) * 8;  // bytes
 
-  auto consume = [&](const u32x4* src, int64_t r0) {
-    // S^T for the two 16-row halves of the tile.  LDS reads run one group of
-    // KG k-steps ahead of the MFMAs that consume them; the two halves and two
-    // k-step parities give four independent accumulation chains.
-    constexpr int KG = KSTEPS % 3 == 0 ? 3 : 4;
-    constexpr int NKG = KSTEPS / KG;
-    static_assert(KSTEPS % KG == 0, "k-step groups must tile D");
-    f32x4 sacc[2][2];
+  auto consume = [&](const u32x4* src, int t, bool more, const int32_t* nids, u32x4* nxt) {
+    // Partial S^T over this wave's half of D: sp[rt][n] for row half rt and
+    // query tile n.  K reads run one group of KG k-steps ahead of the MFMAs.
+    constexpr int KG = KH % 3 == 0 ? 3 : 4;
+    constexpr int NKG = KH / KG;
+    static_assert(KH % KG == 0, "k-step groups must tile half of D");
+    f32x4 sp[2][2];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) sacc[rt][0] = sacc[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 2; ++rt) sp[rt][0] = sp[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 kk[2][2][KG];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
@@ -204,50 +261,82 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
       for (int u = 0; u < KG; ++u)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
-          sacc[rt][u & 1] = mfma16x16x32(as_bf16x8(kk[kg & 1][rt][u]), qf[kg * KG + u], sacc[rt][u & 1]);
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            sp[rt][n] = mfma16x16x32(as_bf16x8(kk[kg & 1][rt][u]), qf[n][kg * KG + u], sp[rt][n]);
+      // The next tile's loads go out between MFMA groups, so a stall on the
+      // memory queue overlaps the MFMAs already issued.
+      if (more && kg < 2) issue_block(t + 2, kg, nids, nxt);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) sacc[rt][0] += sacc[rt][1];
-    // Scores in log2 units, masked by range end and causal horizon.
-    float sc[2][4];
-    float tmax = -INFINITY;
+    // Trade partials with the partner wave (other half of D).  Both partners
+    // form partial(0) + partial(1) with one commutative add, so they hold
+    // bitwise identical scores.
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t j = r0 + rt * 16 + 4 * g + i;
-        const bool vis = q_ok && j < r_end && j < horizon;
-        sc[rt][i] = vis ? sacc[rt][0][i] * sl2 : -INFINITY;
-        tmax = fmaxf(tmax, sc[rt][i]);
-      }
-    tmax = wave_max_xor(tmax, 16);
-    tmax = wave_max_xor(tmax, 32);
-    const float m_new = fmaxf(m2, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
-    float p[2][4];
-    float psum = 0.f;
+      for (int n = 0; n < 2; ++n) xch[w][rt * 2 + n][lane] = sp[rt][n];
+    barrier_keep_loads();
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[rt][i] = __builtin_amdgcn_exp2f(sc[rt][i] - m_use);
-        psum += p[rt][i];
-      }
-    lsum = lsum * alpha + psum;
-    m2 = m_new;
-    if (__ballot(alpha != 1.f)) {
+      for (int n = 0; n < 2; ++n) sp[rt][n] += xch[w ^ 1][rt * 2 + n][lane];
+
+    // Online softmax per query tile.  The exponent reference m2 moves only when
+    // a tile max exceeds it by more than kSlack (log2 units): probabilities stay
+    // below 2^kSlack, the accumulator is rescaled rarely, and acc / l and
+    // lse = m2 + log2(l) do not depend on the reference.
+    u32x4 pp[2];
+    float alpha[2];
+    bool any_rescale = false;
+    // Masking is needed only where some query of the wave sees part of the tile.
+    const bool partial = __ballot(t * 32 + 32 > (vis_lim[0] < vis_lim[1] ? vis_lim[0] : vis_lim[1])) != 0;
 #pragma unroll
-      for (int c = 0; c < CT; ++c) acc[c] *= alpha;
+    for (int n = 0; n < 2; ++n) {
+      float sc[2][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = t * 32 + rt * 16 + 4 * g + i;
+          sc[rt][i] = sp[rt][n][i] * sl2;
+          if (partial && j >= vis_lim[n]) sc[rt][i] = -INFINITY;
+          tmax = fmaxf(tmax, sc[rt][i]);
+        }
+      tmax = max4rows(tmax);
+      const bool grow = tmax > m2[n] + kSlack;
+      const bool rescale = grow && m2[n] > -INFINITY;
+      alpha[n] = rescale ? __builtin_amdgcn_exp2f(m2[n] - tmax) : 1.f;
+      any_rescale |= rescale;
+      if (grow) m2[n] = tmax;
+      const float m_use = m2[n] == -INFINITY ? 0.f : m2[n];
+      float p[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[rt][i] = __builtin_amdgcn_exp2f(sc[rt][i] - m_use);
+          psum += p[rt][i];
+        }
+      lsum[n] = lsum[n] * alpha[n] + psum;
+      pp[n] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
     }
-    const u32x4 pp = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                      pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-    const bf16x8 pB = as_bf16x8(pp);
-    // O^T += V^T P^T; the A operand of column tile ct is read transposed from LDS
-    // (rows rr and 16 + rr, columns 16 ct + 4 (l16 % 4) .. + 3).
+    if (__ballot(any_rescale)) {
+#pragma unroll
+      for (int c = 0; c < CTH; ++c) {
+        acc[c][0] *= alpha[0];
+        acc[c][1] *= alpha[1];
+      }
+    }
+    const bf16x8 pB0 = as_bf16x8(pp[0]), pB1 = as_bf16x8(pp[1]);
+
+    // O^T += V^T P^T for this wave's 16 column tiles; one transposed V read
+    // pair feeds the MFMAs of both query tiles.
     const char* vb = reinterpret_cast<const char*>(src) + v_base;
-    constexpr int CG = 8;  // column tiles per read group
+    constexpr int CG = 4;  // column tiles per read group
     s16x4 vv[2][CG][2];
 #pragma unroll
     for (int u = 0; u < CG; ++u) {
@@ -255,8 +344,8 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
       vv[0][u][1] = lds_read_tr16(vb + T::BLK_IMG * 16 + u * 32);
     }
 #pragma unroll
-    for (int cg = 0; cg < CT / CG; ++cg) {
-      if (cg + 1 < CT / CG) {
+    for (int cg = 0; cg < CTH / CG; ++cg) {
+      if (cg + 1 < CTH / CG) {
 #pragma unroll
         for (int u = 0; u < CG; ++u) {
           const int ct = (cg + 1) * CG + u;
@@ -269,65 +358,95 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
       for (int u = 0; u < CG; ++u) {
         const bf16x8 vA = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(vv[cg & 1][u][0], vv[cg & 1][u][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[cg * CG + u] = mfma16x16x32(vA, pB, acc[cg * CG + u]);
+        acc[cg * CG + u][0] = mfma16x16x32(vA, pB0, acc[cg * CG + u][0]);
+        acc[cg * CG + u][1] = mfma16x16x32(vA, pB1, acc[cg * CG + u][1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // Wait until at most k tiles issued after the current one are still loading.
+  auto wait_tiles = [&](int k) {
+    switch (k * c_w) {
+      case 10: wait_vmcnt<10>(); break;
+      case 9: wait_vmcnt<9>(); break;
+      case 8: wait_vmcnt<8>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+  };
+
+  int win0 = 0;
+  if (n_tiles > 0) {
+    load_ids(0);
+    __syncthreads();
+  }
   int32_t ids[2];
   if (n_tiles > 0) {
-    tile_ids(r_begin, ids);
-    issue(r_begin, ids, lds0);
+    tile_ids(0, win0, ids);
+    issue_block(0, 0, ids, lds0);
+    issue_block(0, 1, ids, lds0);
   }
-  for (int it = 0; it < n_tiles; it += 2) {
-    const bool more1 = it + 1 < n_tiles, more2 = it + 2 < n_tiles;
-    if (more1) tile_ids(r_begin + (int64_t)(it + 1) * 32, ids);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (more1) issue(r_begin + (int64_t)(it + 1) * 32, ids, lds1);
-    consume(lds0, r_begin + (int64_t)it * 32);
-    if (more1) {
-      if (more2) tile_ids(r_begin + (int64_t)(it + 2) * 32, ids);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (more2) issue(r_begin + (int64_t)(it + 2) * 32, ids, lds0);
-      consume(lds1, r_begin + (int64_t)(it + 1) * 32);
+  if (n_tiles > 1) {
+    tile_ids(1, win0, ids);
+    issue_block(1, 0, ids, lds1);
+    issue_block(1, 1, ids, lds1);
+  }
+  // One pipeline step: tile t is consumed from `cur` while tile t + 2 is issued into `nxt`.
+  auto step = [&](int t, const u32x4* cur, u32x4* nxt) {
+    wait_tiles(n_tiles - 1 - t > 0 ? 1 : 0);
+    barrier_keep_loads();
+    const bool more = t + 2 < n_tiles;
+    if (more) {
+      if (2 * (t + 2) + 1 >= win0 + kIdWindow) {  // next window of block ids (drains the loads in flight)
+        win0 = 2 * (t + 2);
+        load_ids(win0);
+        __syncthreads();
+      }
+      tile_ids(t + 2, win0, ids);
     }
+    consume(cur, t, more, ids, nxt);
+  };
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, lds0, lds2);
+    if (t + 1 < n_tiles) step(t + 1, lds1, lds0);
+    if (t + 2 < n_tiles) step(t + 2, lds2, lds1);
   }
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
   const bool bad = flags != 0;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  float lse_v = lsum > 0.f ? (m2 + __log2f(lsum)) * kLn2 : -INFINITY;
-  if (bad) lse_v = NAN;
-
-  if (q_ok) {
-    const int64_t qrow = (int64_t)b * a.n_q + q_lane;
+  float inv[2], lse_v[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    lsum[n] = sum4rows(lsum[n]);
+    inv[n] = lsum[n] > 0.f ? 1.f / lsum[n] : 0.f;
+    lse_v[n] = bad ? NAN : (lsum[n] > 0.f ? (m2[n] + __log2f(lsum[n])) * kLn2 : -INFINITY);
+  }
+  const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    if (!q_ok[n]) continue;
+    const int64_t qrow = (int64_t)b * a.n_q + q_row[n];
+    const int col0 = 256 * dh + 4 * g;
     if (a.direct) {
       if (a.out_bf16) {
-        uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * T::KV + 4 * g;
+        uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * T::KV + col0;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const f32x4 v = bad ? f32x4{NAN, NAN, NAN, NAN} : acc[ct] * inv;
-          uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        for (int ct = 0; ct < CTH; ++ct) {
+          const f32x4 v = bad ? nan4 : acc[ct][n] * inv[n];
+          const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<uint2*>(o + 16 * ct) = pk;
         }
       } else {
-        float* o = static_cast<float*>(a.out) + qrow * T::KV + 4 * g;
+        float* o = static_cast<float*>(a.out) + qrow * T::KV + col0;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? f32x4{NAN, NAN, NAN, NAN} : acc[ct] * inv;
+        for (int ct = 0; ct < CTH; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv[n];
       }
-      if (a.lse && g == 0) a.lse[qrow] = lse_v;
+      if (a.lse && dh == 0 && g == 0) a.lse[qrow] = lse_v[n];
     } else {
-      const int64_t prow = ((int64_t)b * a.splits + s) * a.n_q + q_lane;
-      float* o = a.o_part + prow * T::KV + 4 * g;
+      const int64_t prow = ((int64_t)b * a.splits + s) * a.n_q + q_row[n];
+      float* o = a.o_part + prow * T::KV + col0;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? f32x4{NAN, NAN, NAN, NAN} : acc[ct] * inv;
-      if (g == 0) a.lse_part[prow] = lse_v;
+      for (int ct = 0; ct < CTH; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv[n];
+      if (dh == 0 && g == 0) a.lse_part[prow] = lse_v[n];
     }
   }
   if (tid == 0) a.status[item] = flags;

@@ -33,9 +33,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// Two floats -> packed pair of bfloat16 (RNE) in one dword, lo = a.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed pair of bfloat16 in one dword, lo = a: one hardware
+// conversion (round to nearest even, NaN stays NaN).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Reinterpret four dwords as eight bfloat16 MFMA operand lanes.
@@ -88,8 +92,46 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_wave_base), 16, voff, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (base, size in bytes) as four scalar words.
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r = {(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
+  return r;
+}
+
+// LDS byte address of a __shared__ object (32-bit local address space).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)(p));
+}
+
+// Asynchronous 16-byte copy per lane, buffer offset `voff` -> LDS (wave base + 16 * lane);
+// offsets at or past the resource size deliver zeros.  Issued as inline assembly so the
+// compiler does not track it: the caller orders it with explicit vmcnt waits.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_wave_base, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
+      : "memory", "m0");
+}
+
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows
+// holding one MFMA output column), with the row-swapping permlane instructions.
+__device__ __forceinline__ float max4rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float sum4rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 }  // namespace mla
