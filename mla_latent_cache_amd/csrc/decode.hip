@@ -8,21 +8,23 @@
 // lse = log sum_j exp(s_j).
 //
 // Schedule.  The rows of a request are cut into `splits` ranges of whole cache
-// blocks.  One workgroup handles one (request, range, tile of 64 query rows)
-// and walks its range 32 rows (two 16-row cache blocks) at a time:
+// blocks.  One workgroup of eight waves handles one (request, range, tile of 64
+// query rows) and walks its range 32 rows (two 16-row cache blocks) at a time:
 //   * blocks go HBM -> LDS directly (buffer_load ... lds), one buffer resource
 //     per block, so rows past the request's end read as zeros and no address
-//     outside a real block is formed; a ring of three tile buffers keeps two
-//     tiles in flight while one is consumed;
-//   * wave (qh, dh) owns query rows [32 qh, 32 qh + 32) of the tile and half
-//     dh of the row width: it computes the partial S^T = K Q^T over its half
-//     of D with 16x16x32 bf16 MFMA (every K read from LDS feeds two MFMAs),
-//     trades partials with its partner wave through LDS, and both partners
-//     then hold the same full scores and run the same online softmax;
-//   * P^T is already in the B-operand layout of O^T = V^T P^T; wave (qh, dh)
-//     accumulates output columns [256 dh, 256 dh + 256) for its 32 query rows,
-//     reading V^T from the same LDS tile with the transposing ds_read_b64_tr_b16
-//     (again one read per two MFMAs).
+//     outside a real block is formed; a ring of three tile buffers keeps the
+//     next tile loading while one is consumed;
+//   * wave (qh, dq) computes the partial S^T = K Q^T of query rows
+//     [32 qh, 32 qh + 32) over its quarter dq of the row width with 16x16x32
+//     bf16 MFMA, the K operand read as two 8-byte LDS reads per lane;
+//   * the partials are summed through LDS so that each wave owns eight query
+//     rows for the online softmax; it publishes bf16 P^T, already in the
+//     B-operand layout of O^T = V^T P^T, and the per-query rescale factor;
+//   * wave (qh, dq) then accumulates output columns [128 dq, 128 dq + 128) of
+//     its 32 query rows, reading V^T from the same LDS tile with the
+//     transposing ds_read_b64_tr_b16; this PV step of tile t runs in the same
+//     phase as the S step of tile t + 1.
+// Two waves share each SIMD, so one wave's LDS reads overlap the other's MFMAs.
 // With one range per request the workgroup writes the final output and LSE;
 // otherwise it writes (o, lse) partials and decode_merge combines them:
 //   M = max_s lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
@@ -87,7 +89,6 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int kIdWindow = 512;  // cache-block ids of a range staged in LDS at a time
 constexpr float kSlack = 8.f;   // log2 headroom before the softmax reference moves
 
 // ---------------------------------------------------------------------------
@@ -98,27 +99,33 @@ struct Tile {
   static constexpr int KV = 512;
   static constexpr int D = KV + D_ROPE;
   static constexpr int CH = D / 8;                         // 16-byte chunks per row
-  static constexpr int STRIDE = CH + 2;                    // LDS row stride: 8 * odd dwords
+  static constexpr int STRIDE = CH + 2;                    // LDS row pitch in chunks: 8 * odd dwords
   static constexpr int BLK_POS = 16 * STRIDE;              // chunk slots of one block image
   static constexpr int BLK_IMG = (BLK_POS + 63) / 64 * 64; // whole wave-loads per block
   static constexpr int BLK_LOADS = BLK_IMG / 64;
   static constexpr int IMG = 2 * BLK_IMG;                  // one 32-row tile
+  static constexpr int TILE_LOADS = 2 * BLK_LOADS;         // 1 KB wave-loads per tile
+  static constexpr int WAVE_LOADS = (TILE_LOADS + 7) / 8;  // per wave and tile (at most)
   static constexpr int KSTEPS = D / 32;                    // 32-wide k-steps of S
-  static constexpr int KH = KSTEPS / 2;                    // k-steps per half of D
-  static constexpr int CTH = KV / 32;                      // 16-column output tiles per half
-  static_assert((STRIDE * 4) % 16 == 8, "row stride must be 8 * odd dwords");
-  static_assert(KSTEPS % 2 == 0, "D must split into two halves of whole k-steps");
+  static constexpr int KQ = (KSTEPS + 3) / 4;              // k-steps of the largest D quarter
+  static constexpr int CT = 8;                             // 16-column output tiles per quarter
+  static_assert((STRIDE * 4) % 16 == 8, "row pitch must be 8 * odd dwords");
+  static_assert(KSTEPS >= 16 && KSTEPS <= 20, "four k-steps per quarter plus a partial fifth");
 };
 
 template <int D_ROPE>
-__global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) {
+__global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) {
   using T = Tile<D_ROPE>;
-  constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KH = T::KH, CTH = T::CTH;
-  __shared__ __attribute__((aligned(16))) u32x4 lds0[T::IMG];
-  __shared__ __attribute__((aligned(16))) u32x4 lds1[T::IMG];
-  __shared__ __attribute__((aligned(16))) u32x4 lds2[T::IMG];
-  __shared__ __attribute__((aligned(16))) f32x4 xch[4][4][64];  // S partials: [wave][rt * 2 + n][lane]
-  __shared__ int32_t id_lds[kIdWindow];
+  constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KQ = T::KQ, CT = T::CT;
+  // Exchange planes are 64 lanes x 8 bytes, padded to 576 bytes so that the
+  // softmax-layout reads (8 lanes per 64-byte run, runs 128 bytes apart,
+  // consecutive planes) spread over all banks.
+  constexpr int PLANE = 72;  // plane pitch in 8-byte units
+  __shared__ __attribute__((aligned(16))) u32x4 ring[3 * T::IMG];  // three tile buffers
+  __shared__ __attribute__((aligned(16))) uint2 xs[8][2][4][PLANE];  // S partials [wave][half][n * 2 + rt][lane]
+  __shared__ __attribute__((aligned(16))) uint2 pb[2][2][2][PLANE];  // bf16 P^T [qh][n][rt][lane]
+  __shared__ float al[64];                                           // per-query rescale of the output
+  __shared__ float fin[64];                                          // per-query 1 / l at the end
 
   write_header(a);
   int b, s, mt, item;
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int qh = w >> 1, dh = w & 1;
+  const int qh = w & 1, dq = w >> 1;                       // query half, D / column quarter
   const int l16 = lane & 15, g = lane >> 4;
 
   const int64_t L = a.seq_lens[b];
@@ -136,317 +143,307 @@ __global__ __launch_bounds__(256, 1) void decode_split_mfma(const DecodeArgs a) 
   if (flags || r_end > L) r_end = flags ? r_begin : L;
   const int n_tiles = r_end > r_begin ? (int)((r_end - r_begin + 31) / 32) : 0;
 
-  // The lane's query rows in the wave's two 16-row tiles n = 0, 1, and how
-  // many rows of the range each of them sees (range end and causal horizon).
-  int q_row[2], vis_lim[2];
+  // Matrix layout: lane (l16, g) of query tile n works on query row
+  // 32 qh + 16 n + l16 of the workgroup's 64.
+  int q_row[2];
   bool q_ok[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     q_row[n] = mt * kQRowsPerWG + 32 * qh + 16 * n + l16;
     q_ok[n] = q_row[n] < a.n_q;
-    const int64_t horizon = L - a.t_q + (q_ok[n] ? q_row[n] / a.n_head : 0) + 1;
+  }
+  // Softmax layout: lane (qi, rt, g) = bits (0..2, 3, 4..5) owns query row
+  // fq = 32 qh + 16 (dq / 2) + 8 (dq % 2) + qi and tile rows 16 rt + 4 g + i.
+  const int qi = lane & 7, rt_f = (lane >> 3) & 1, g_f = lane >> 4;
+  const int nf = dq >> 1, hf = dq & 1;
+  const int fq = 32 * qh + 16 * nf + 8 * hf + qi;
+  const int src_lane = g_f * 16 + 8 * hf + qi;  // same query and rows in the matrix layout
+  int vis_lim;
+  {
+    const int qr = mt * kQRowsPerWG + fq;
+    const bool ok = qr < a.n_q;
+    const int64_t horizon = L - a.t_q + (ok ? qr / a.n_head : 0) + 1;
     const int64_t vis_end = horizon < r_end ? horizon : r_end;
-    vis_lim[n] = !q_ok[n] || vis_end <= r_begin ? 0 : (int)(vis_end - r_begin);
+    vis_lim = !ok || vis_end <= r_begin ? 0 : (int)(vis_end - r_begin);
   }
 
-  // B operand of S^T: absorbed queries of both tiles over this wave's half of D.
-  bf16x8 qf[2][KH];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + q_row[n]) * D +
-                         32 * KH * dh + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < KH; ++kk)
-      qf[n][kk] = q_ok[n] ? *reinterpret_cast<const bf16x8*>(qp + 32 * kk) : zero_bf16x8();
-  }
-  wait_vmcnt<0>();  // queries resident before the tile loop (keeps its waits exact)
+  // B operand of S^T for this wave's k-steps kk = dq + 4 j.  The lane's eight
+  // k slots are columns 32 kk + 4 g + {0..3} and 32 kk + 16 + 4 g + {0..3}: the
+  // K operand is then two 8-byte LDS reads per lane, 32 bytes apart.
+  const int nk = (T::KSTEPS - dq + 3) / 4;
+  bf16x8 qf[2][KQ];
   const float sl2 = a.scale * kLog2e;
 
-  f32x4 acc[CTH][2];
+  f32x4 acc[CT][2];
 #pragma unroll
-  for (int c = 0; c < CTH; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  for (int c = 0; c < CT; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2 = -INFINITY, lsum = 0.f;  // softmax state of query fq (log2 units)
 
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
   const int32_t* bt_row = a.bt + (int64_t)b * a.max_blocks;
 
-  // Block ids of the range are staged in LDS, kIdWindow at a time, so the loop
-  // reads them without a vector-memory wait (which would also wait for the
-  // tiles in flight).  Tile t uses range-relative slots 2t and 2t + 1.
+  // Block ids come from the table through scalar loads (which do not touch
+  // the vector-memory counter the tile waits use), fetched one phase before
+  // they are needed.  Tile t uses range-relative slots 2t and 2t + 1.
   const int slot0 = s * a.chunk_blocks;
   const int nslots = (int)((r_end - r_begin + 15) / 16);
-  auto load_ids = [&](int win0) {
-    for (int i = tid; i < kIdWindow; i += 256) {
-      const int rel = win0 + i;
-      id_lds[i] = rel < nslots ? bt_row[slot0 + rel] : -1;
+  // (The table is read-only for the whole call, so the scalar cache may hold it.)
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  const_i32* bt_s = (const_i32*)(bt_row + slot0);
+  auto tile_ids = [&](int t, int32_t* ids) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int rel = 2 * t + hb;
+      ids[hb] = rel < nslots ? bt_s[rel] : -1;
     }
   };
-  auto tile_ids = [&](int t, int win0, int32_t* ids) {
-    ids[0] = __builtin_amdgcn_readfirstlane(id_lds[2 * t - win0]);
-    ids[1] = __builtin_amdgcn_readfirstlane(id_lds[2 * t + 1 - win0]);
-  };
 
-  // This wave's share of the 64-chunk wave-loads of one block image, as byte
-  // offsets into the block (the same for every block).  Rows 8..15 of a block
-  // swap the two 16-byte chunks of each 32-byte pair (bank spreading).
-  constexpr int WAVE_LOADS = (T::BLK_LOADS + 3) / 4;
-  uint32_t voffs[WAVE_LOADS];
+  // This wave's share of the 1 KB wave-loads of a tile image: load u = w + 8 j
+  // covers chunk slots [64 u, 64 u + 64) of the image, i.e. block u / BLK_LOADS.
+  // Rows 8..15 of a block swap the two 16-byte chunks of each 32-byte pair
+  // (bank spreading); slots past a row's end are padding.
+  uint32_t voffs[T::WAVE_LOADS];
+  int c_w = 0;  // this wave's loads per tile (for the vmcnt waits)
 #pragma unroll
-  for (int u = 0; u < WAVE_LOADS; ++u) {
-    const int pos = (w + 4 * u) * 64 + lane;
+  for (int j = 0; j < T::WAVE_LOADS; ++j) {
+    const int u = w + 8 * j;
+    const int hb = u / T::BLK_LOADS;
+    const int pos = (u - hb * T::BLK_LOADS) * 64 + lane;
     const int rl = pos / STRIDE;
     const int cp = pos - rl * STRIDE;
-    voffs[u] = (rl < 16 && cp < CH) ? (uint32_t)(rl * D + ((cp ^ ((rl >> 3) & 1)) * 8)) * 2u : 0x7ffffff0u;
+    voffs[j] = (rl < 16 && cp < CH) ? (uint32_t)(rl * D + ((cp ^ ((rl >> 3) & 1)) * 8)) * 2u : 0x7ffffff0u;
+    c_w += u < T::TILE_LOADS ? 1 : 0;
   }
-  int c_w = 0;  // this wave's buffer loads per tile (for the vmcnt waits)
-#pragma unroll
-  for (int u = 0; u < WAVE_LOADS; ++u) c_w += (w + 4 * u < T::BLK_LOADS) ? 2 : 0;
 
-  // Issue the loads of block hb (0 or 1) of tile t (block ids `ids`) into buffer `dst`.
-  auto issue_block = [&](int t, int hb, const int32_t* ids, u32x4* dst) {
-    const int64_t r0 = r_begin + (int64_t)t * 32;
-    {
-      const int64_t left = r_end - (r0 + hb * 16);
-      const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+  // Issue the loads of tile t (block ids `ids`) into `dst`.
+  auto issue_tile = [&](int t, const int32_t* ids, u32x4* dst) {
+    i32x4 rs[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
       const int32_t id = ids[hb];
+      const int64_t left = r_end - (r_begin + (int64_t)t * 32 + hb * 16);
+      const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
       const bool ok = id >= 0 && (int64_t)id < a.num_blocks;
       if (nvalid > 0 && !ok) flags |= kBadBlock;
       const uint16_t* base = ok ? kv + (int64_t)id * 16 * D : kv;
-      const i32x4 rs = raw_rsrc(base, ok ? (uint32_t)(nvalid * D * 2) : 0u);
-      const uint32_t lbase = lds_addr(dst + hb * T::BLK_IMG);
+      rs[hb] = raw_rsrc(base, ok ? (uint32_t)(nvalid * D * 2) : 0u);
+    }
+    const uint32_t lbase = lds_addr(dst);
 #pragma unroll
-      for (int u = 0; u < WAVE_LOADS; ++u) {
-        if (w + 4 * u < T::BLK_LOADS) dma16(rs, lbase + (uint32_t)((w + 4 * u) * 64 * 16), voffs[u]);
-      }
+    for (int j = 0; j < T::WAVE_LOADS; ++j) {
+      const int u = w + 8 * j;
+      if (u < T::TILE_LOADS) dma16(u < T::BLK_LOADS ? rs[0] : rs[1], lbase + (uint32_t)u * 1024u, voffs[j]);
     }
   };
 
-  // Per-lane LDS offsets.  Tile row r, chunk c lives at chunk slot
-  // (r / 16) * BLK_IMG + (r % 16) * STRIDE + (c ^ sw), sw = ((r % 16) >> 3) & 1;
-  // sw only flips bit 0, so every address below is a lane base plus a constant.
-  // K (A operand of S^T) for k-step kk of half dh: row l16 (+16 rt), chunk 4 (KH dh + kk) + g.
+  // Per-lane LDS byte offsets within a tile image.  Tile row r, chunk c lives
+  // at chunk slot (r / 16) * BLK_IMG + (r % 16) * STRIDE + (c ^ sw) with
+  // sw = ((r % 16) >> 3) & 1, which only flips bit 0 of the chunk.
+  // K (A operand of S^T), k-step kk, block rt: row l16, bytes 64 kk + 8 g and +32.
   const int sw_k = (l16 >> 3) & 1;
-  const int k_base = l16 * STRIDE + ((4 * KH * dh + g) ^ sw_k);
-  // V^T (A operand of O^T) for column tile ct of half dh: rows rr and 16 + rr,
-  // columns 256 dh + 16 ct + 4 (l16 % 4) .. + 3.
+  const int k_off = (l16 * STRIDE + ((g >> 1) ^ sw_k)) * 16 + (g & 1) * 8 + 64 * dq;
+  // V^T (A operand of O^T) for column tile ct of quarter dq: rows rr and 16 + rr,
+  // columns 128 dq + 16 ct + 4 (l16 % 4) .. + 3.
   const int rr = 4 * g + (l16 >> 2);
   const int sw_v = (rr >> 3) & 1;
-  const int v_base = (rr * STRIDE + ((32 * dh + ((l16 & 3) >> 1)) ^ sw_v)) * 16 + (l16 & 1) * 8;  // bytes
+  const int v_off = (rr * STRIDE + ((16 * dq + ((l16 & 3) >> 1)) ^ sw_v)) * 16 + (l16 & 1) * 8;
 
-  auto consume = [&](const u32x4* src, int t, bool more, const int32_t* nids, u32x4* nxt) {
-    // Partial S^T over this wave's half of D: sp[rt][n] for row half rt and
-    // query tile n.  K reads run one group of KG k-steps ahead of the MFMAs.
-    constexpr int KG = KH % 3 == 0 ? 3 : 4;
-    constexpr int NKG = KH / KG;
-    static_assert(KH % KG == 0, "k-step groups must tile half of D");
+  // O^T += V^T P^T for tile image `img`, after rescaling by the factors the
+  // softmax step published with P.
+  auto pv = [&](const u32x4* img) {
+    const uint2 p00 = pb[qh][0][0][lane], p01 = pb[qh][0][1][lane];
+    const uint2 p10 = pb[qh][1][0][lane], p11 = pb[qh][1][1][lane];
+    const bf16x8 pB0 = as_bf16x8(u32x4{p00.x, p00.y, p01.x, p01.y});
+    const bf16x8 pB1 = as_bf16x8(u32x4{p10.x, p10.y, p11.x, p11.y});
+    const float al0 = al[32 * qh + l16], al1 = al[32 * qh + 16 + l16];
+    if (__ballot(al0 != 1.f || al1 != 1.f)) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        acc[c][0] *= al0;
+        acc[c][1] *= al1;
+      }
+    }
+    const char* vb = reinterpret_cast<const char*>(img) + v_off;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const s16x4 v0 = lds_read_tr16(vb + ct * 32);
+      const s16x4 v1 = lds_read_tr16(vb + T::BLK_IMG * 16 + ct * 32);
+      const bf16x8 vA = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[ct][0] = mfma16x16x32(vA, pB0, acc[ct][0]);
+      acc[ct][1] = mfma16x16x32(vA, pB1, acc[ct][1]);
+    }
+  };
+
+  // Partial S^T of tile image `img` over this wave's k-steps, to xs[w].
+  auto s_part = [&](const u32x4* img) {
     f32x4 sp[2][2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) sp[rt][0] = sp[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 kk[2][2][KG];
+    const char* kb = reinterpret_cast<const char*>(img) + k_off;
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+      if (j < 4 || j < nk) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(kb + rt * T::BLK_IMG * 16 + 256 * j);
+          const uint2 hi = *reinterpret_cast<const uint2*>(kb + rt * T::BLK_IMG * 16 + 256 * j + 32);
+          const bf16x8 kA = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+          sp[rt][0] = mfma16x16x32(kA, qf[0][j], sp[rt][0]);
+          sp[rt][1] = mfma16x16x32(kA, qf[1][j], sp[rt][1]);
+        }
+      }
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int u = 0; u < KG; ++u) kk[0][rt][u] = src[rt * T::BLK_IMG + k_base + 4 * u];
-#pragma unroll
-    for (int kg = 0; kg < NKG; ++kg) {
-      if (kg + 1 < NKG) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int u = 0; u < KG; ++u)
-            kk[(kg + 1) & 1][rt][u] = src[rt * T::BLK_IMG + k_base + 4 * ((kg + 1) * KG + u)];
+      for (int n = 0; n < 2; ++n) {
+        xs[w][0][n * 2 + rt][lane] = uint2{__float_as_uint(sp[rt][n][0]), __float_as_uint(sp[rt][n][1])};
+        xs[w][1][n * 2 + rt][lane] = uint2{__float_as_uint(sp[rt][n][2]), __float_as_uint(sp[rt][n][3])};
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < KG; ++u)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int n = 0; n < 2; ++n)
-            sp[rt][n] = mfma16x16x32(as_bf16x8(kk[kg & 1][rt][u]), qf[n][kg * KG + u], sp[rt][n]);
-      // The next tile's loads go out between MFMA groups, so a stall on the
-      // memory queue overlaps the MFMAs already issued.
-      if (more && kg < 2) issue_block(t + 2, kg, nids, nxt);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Trade partials with the partner wave (other half of D).  Both partners
-    // form partial(0) + partial(1) with one commutative add, so they hold
-    // bitwise identical scores.
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) xch[w][rt * 2 + n][lane] = sp[rt][n];
-    barrier_keep_loads();
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) sp[rt][n] += xch[w ^ 1][rt * 2 + n][lane];
-
-    // Online softmax per query tile.  The exponent reference m2 moves only when
-    // a tile max exceeds it by more than kSlack (log2 units): probabilities stay
-    // below 2^kSlack, the accumulator is rescaled rarely, and acc / l and
-    // lse = m2 + log2(l) do not depend on the reference.
-    u32x4 pp[2];
-    float alpha[2];
-    bool any_rescale = false;
-    // Masking is needed only where some query of the wave sees part of the tile.
-    const bool partial = __ballot(t * 32 + 32 > (vis_lim[0] < vis_lim[1] ? vis_lim[0] : vis_lim[1])) != 0;
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float sc[2][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = t * 32 + rt * 16 + 4 * g + i;
-          sc[rt][i] = sp[rt][n][i] * sl2;
-          if (partial && j >= vis_lim[n]) sc[rt][i] = -INFINITY;
-          tmax = fmaxf(tmax, sc[rt][i]);
-        }
-      tmax = max4rows(tmax);
-      const bool grow = tmax > m2[n] + kSlack;
-      const bool rescale = grow && m2[n] > -INFINITY;
-      alpha[n] = rescale ? __builtin_amdgcn_exp2f(m2[n] - tmax) : 1.f;
-      any_rescale |= rescale;
-      if (grow) m2[n] = tmax;
-      const float m_use = m2[n] == -INFINITY ? 0.f : m2[n];
-      float p[2][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[rt][i] = __builtin_amdgcn_exp2f(sc[rt][i] - m_use);
-          psum += p[rt][i];
-        }
-      lsum[n] = lsum[n] * alpha[n] + psum;
-      pp[n] = u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                    pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-    }
-    if (__ballot(any_rescale)) {
-#pragma unroll
-      for (int c = 0; c < CTH; ++c) {
-        acc[c][0] *= alpha[0];
-        acc[c][1] *= alpha[1];
-      }
-    }
-    const bf16x8 pB0 = as_bf16x8(pp[0]), pB1 = as_bf16x8(pp[1]);
-
-    // O^T += V^T P^T for this wave's 16 column tiles; one transposed V read
-    // pair feeds the MFMAs of both query tiles.
-    const char* vb = reinterpret_cast<const char*>(src) + v_base;
-    constexpr int CG = 4;  // column tiles per read group
-    s16x4 vv[2][CG][2];
-#pragma unroll
-    for (int u = 0; u < CG; ++u) {
-      vv[0][u][0] = lds_read_tr16(vb + u * 32);
-      vv[0][u][1] = lds_read_tr16(vb + T::BLK_IMG * 16 + u * 32);
-    }
-#pragma unroll
-    for (int cg = 0; cg < CTH / CG; ++cg) {
-      if (cg + 1 < CTH / CG) {
-#pragma unroll
-        for (int u = 0; u < CG; ++u) {
-          const int ct = (cg + 1) * CG + u;
-          vv[(cg + 1) & 1][u][0] = lds_read_tr16(vb + ct * 32);
-          vv[(cg + 1) & 1][u][1] = lds_read_tr16(vb + T::BLK_IMG * 16 + ct * 32);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < CG; ++u) {
-        const bf16x8 vA = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(vv[cg & 1][u][0], vv[cg & 1][u][1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[cg * CG + u][0] = mfma16x16x32(vA, pB0, acc[cg * CG + u][0]);
-        acc[cg * CG + u][1] = mfma16x16x32(vA, pB1, acc[cg * CG + u][1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
   };
 
-  // Wait until at most k tiles issued after the current one are still loading.
-  auto wait_tiles = [&](int k) {
-    switch (k * c_w) {
-      case 10: wait_vmcnt<10>(); break;
-      case 9: wait_vmcnt<9>(); break;
-      case 8: wait_vmcnt<8>(); break;
-      default: wait_vmcnt<0>(); break;
+  // Full scores of tile t for this lane's query and rows (sum of the four
+  // quarter partials), online softmax, and P^T / rescale factors published to
+  // LDS for the PV step.  The exponent reference m2 moves only when a tile max
+  // exceeds it by more than kSlack (log2 units): probabilities stay below
+  // 2^kSlack, the output is rescaled rarely, and acc / l and lse = m2 + log2(l)
+  // do not depend on the reference.
+  auto softmax = [&](int t) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint2 lo = xs[qh + 2 * d][0][nf * 2 + rt_f][src_lane];
+      const uint2 hi = xs[qh + 2 * d][1][nf * 2 + rt_f][src_lane];
+      sc += f32x4{__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(hi.x), __uint_as_float(hi.y)};
     }
+    const int j0 = t * 32 + 16 * rt_f + 4 * g_f;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = j0 + i < vis_lim ? sc[i] * sl2 : -INFINITY;
+      tmax = fmaxf(tmax, sc[i]);
+    }
+    tmax = fmaxf(tmax, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                                     0, __builtin_bit_cast(int, tmax), 0x128, 0xf, 0xf, false)));
+    tmax = max4rows(tmax);
+    const bool grow = tmax > m2 + kSlack;
+    const float alpha = grow && m2 > -INFINITY ? __builtin_amdgcn_exp2f(m2 - tmax) : 1.f;
+    if (grow) m2 = tmax;
+    const float m_use = m2 == -INFINITY ? 0.f : m2;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    const uint2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    pb[qh][nf][rt_f][src_lane] = pk;
+    if (lane < 8) al[fq] = alpha;
   };
 
-  int win0 = 0;
-  if (n_tiles > 0) {
-    load_ids(0);
-    __syncthreads();
-  }
+  // Prologue: tile 0's loads go out first, then the queries, then tile 1; the
+  // wait leaves only tile 1 in flight.
   int32_t ids[2];
   if (n_tiles > 0) {
-    tile_ids(0, win0, ids);
-    issue_block(0, 0, ids, lds0);
-    issue_block(0, 1, ids, lds0);
+    tile_ids(0, ids);
+    issue_tile(0, ids, ring);
   }
-  if (n_tiles > 1) {
-    tile_ids(1, win0, ids);
-    issue_block(1, 0, ids, lds1);
-    issue_block(1, 1, ids, lds1);
-  }
-  // One pipeline step: tile t is consumed from `cur` while tile t + 2 is issued into `nxt`.
-  auto step = [&](int t, const u32x4* cur, u32x4* nxt) {
-    wait_tiles(n_tiles - 1 - t > 0 ? 1 : 0);
-    barrier_keep_loads();
-    const bool more = t + 2 < n_tiles;
-    if (more) {
-      if (2 * (t + 2) + 1 >= win0 + kIdWindow) {  // next window of block ids (drains the loads in flight)
-        win0 = 2 * (t + 2);
-        load_ids(win0);
-        __syncthreads();
-      }
-      tile_ids(t + 2, win0, ids);
-    }
-    consume(cur, t, more, ids, nxt);
-  };
-  for (int t = 0; t < n_tiles; t += 3) {
-    step(t, lds0, lds2);
-    if (t + 1 < n_tiles) step(t + 1, lds1, lds0);
-    if (t + 2 < n_tiles) step(t + 2, lds2, lds1);
-  }
-
-  const bool bad = flags != 0;
-  float inv[2], lse_v[2];
+  // Queries: B operand of S^T for this wave's k-steps (see qf).
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
-    lsum[n] = sum4rows(lsum[n]);
-    inv[n] = lsum[n] > 0.f ? 1.f / lsum[n] : 0.f;
-    lse_v[n] = bad ? NAN : (lsum[n] > 0.f ? (m2[n] + __log2f(lsum[n])) * kLn2 : -INFINITY);
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + q_row[n]) * D + 32 * dq + 4 * g;
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q_ok[n] && j < nk) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(qp + 128 * j);
+        const uint2 hi = *reinterpret_cast<const uint2*>(qp + 128 * j + 16);
+        v = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      qf[n][j] = as_bf16x8(v);
+    }
   }
+  if (n_tiles > 1) {
+    tile_ids(1, ids);
+    issue_tile(1, ids, ring + T::IMG);
+    switch (c_w) {
+      case 5: wait_vmcnt<5>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+  } else {
+    wait_vmcnt<0>();
+  }
+  if (n_tiles > 0) barrier_keep_loads();
+  int cur = 0;  // ring slot of tile t
+  for (int t = 0; t < n_tiles; ++t) {
+    const int prev = cur == 0 ? 2 : cur - 1, nxt2 = prev;  // tile t + 2 reuses tile t - 1's slot
+    const bool more = t + 2 < n_tiles;
+    if (more) tile_ids(t + 2, ids);  // scalar loads, complete by the barrier below
+    if (t > 0) pv(ring + prev * T::IMG);
+    s_part(ring + cur * T::IMG);
+    barrier_keep_loads();  // partials visible; tile t - 1 no longer read
+    if (more) issue_tile(t + 2, ids, ring + nxt2 * T::IMG);
+    softmax(t);
+    if (t + 1 < n_tiles) {  // tile t + 1 resident
+      if (more) {
+        switch (c_w) {
+          case 5: wait_vmcnt<5>(); break;
+          case 4: wait_vmcnt<4>(); break;
+          default: wait_vmcnt<0>(); break;
+        }
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    barrier_keep_loads();  // P^T and rescale factors visible
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  if (n_tiles > 0) pv(ring + (cur == 0 ? 2 : cur - 1) * T::IMG);
+
+  // Final normalisation: the owner lanes of each query sum their partial l,
+  // publish 1 / l, and write the LSE.
+  const bool bad = flags != 0;
+  lsum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, lsum), 0x128, 0xf, 0xf, false));
+  lsum = sum4rows(lsum);
+  if (lane < 8) {
+    fin[fq] = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int qr = mt * kQRowsPerWG + fq;
+    if (qr < a.n_q) {
+      const float lse_v = bad ? NAN : (lsum > 0.f ? (m2 + __log2f(lsum)) * kLn2 : -INFINITY);
+      if (a.direct) {
+        if (a.lse) a.lse[(int64_t)b * a.n_q + qr] = lse_v;
+      } else {
+        a.lse_part[((int64_t)b * a.splits + s) * a.n_q + qr] = lse_v;
+      }
+    }
+  }
+  __syncthreads();
   const f32x4 nan4 = {NAN, NAN, NAN, NAN};
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     if (!q_ok[n]) continue;
-    const int64_t qrow = (int64_t)b * a.n_q + q_row[n];
-    const int col0 = 256 * dh + 4 * g;
+    const float inv = fin[32 * qh + 16 * n + l16];
+    const int col0 = 128 * dq + 4 * g;
     if (a.direct) {
+      const int64_t qrow = (int64_t)b * a.n_q + q_row[n];
       if (a.out_bf16) {
         uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * T::KV + col0;
 #pragma unroll
-        for (int ct = 0; ct < CTH; ++ct) {
-          const f32x4 v = bad ? nan4 : acc[ct][n] * inv[n];
+        for (int ct = 0; ct < CT; ++ct) {
+          const f32x4 v = bad ? nan4 : acc[ct][n] * inv;
           const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<uint2*>(o + 16 * ct) = pk;
         }
       } else {
         float* o = static_cast<float*>(a.out) + qrow * T::KV + col0;
 #pragma unroll
-        for (int ct = 0; ct < CTH; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv[n];
+        for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv;
       }
-      if (a.lse && dh == 0 && g == 0) a.lse[qrow] = lse_v[n];
     } else {
       const int64_t prow = ((int64_t)b * a.splits + s) * a.n_q + q_row[n];
       float* o = a.o_part + prow * T::KV + col0;
 #pragma unroll
-      for (int ct = 0; ct < CTH; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv[n];
-      if (dh == 0 && g == 0) a.lse_part[prow] = lse_v[n];
+      for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv;
     }
   }
   if (tid == 0) a.status[item] = flags;
@@ -543,56 +540,70 @@ __global__ __launch_bounds__(128) void decode_split_generic(const DecodeArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the split partials: one workgroup of 128 threads per query row.
+// Merge of the split partials: one wave per query row, four rows per workgroup.
+// Lane l owns output columns 4 l + 256 j; the split loop is unrolled by eight
+// so each lane has up to sixteen 16-byte partial loads in flight.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void decode_merge(const DecodeArgs a) {
-  __shared__ float wts[kMaxSplits];
-  __shared__ float red[2];
-  const int64_t qrow = blockIdx.x;  // b * n_q + q
+constexpr int kMergeRows = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t qrow = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);  // b * n_q + q
+  if (qrow >= (int64_t)a.batch * a.n_q) return;
   const int b = (int)(qrow / a.n_q);
   const int q = (int)(qrow - (int64_t)b * a.n_q);
-  const int tid = threadIdx.x;
   const int S = a.splits, R = a.kv_rank;
-  const float* lp = a.lse_part + (int64_t)b * S * a.n_q + q;
+  const float* lp = a.lse_part + (int64_t)b * S * a.n_q + q;  // split k at lp[k * n_q]
 
   float mx = -INFINITY;
   bool nan_seen = false;
-  for (int k = tid; k < S; k += 128) {
+  for (int k = lane; k < S; k += 64) {
     const float v = lp[(int64_t)k * a.n_q];
     nan_seen |= isnan(v);
     mx = fmaxf(mx, v);
   }
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  const int any_nan = __syncthreads_or(nan_seen ? 1 : 0);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(red[0], red[1]);
-  __syncthreads();
-
-  float wsum_part = 0.f;
-  for (int k = tid; k < S; k += 128) {
-    const float wk = M == -INFINITY ? 0.f : expf(lp[(int64_t)k * a.n_q] - M);
-    wts[k] = wk;
-    wsum_part += wk;
-  }
-  for (int off = 32; off > 0; off >>= 1) wsum_part += __shfl_xor(wsum_part, off, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = wsum_part;
-  __syncthreads();
-  const float wsum = red[0] + red[1];
+  const float M = wave_max(mx);
+  const bool any_nan = __ballot(nan_seen) != 0;
+  float wpart = 0.f;
+  if (M != -INFINITY)
+    for (int k = lane; k < S; k += 64) wpart += __expf(lp[(int64_t)k * a.n_q] - M);
+  const float wsum = wave_sum(wpart);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
   const float* op = a.o_part + ((int64_t)b * S * a.n_q + q) * R;
   const int64_t sstride = (int64_t)a.n_q * R;
-  for (int c0 = tid * 4; c0 < R; c0 += 128 * 4) {
+  for (int c0 = 4 * lane; c0 < R; c0 += 256) {
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (R - c0 >= 4) {
-      for (int k = 0; k < S; ++k) {
-        const float wk = wts[k];
-        if (wk != 0.f) o += wk * *reinterpret_cast<const f32x4*>(op + k * sstride + c0);
+    if (M != -INFINITY) {
+      if (R - c0 >= 4) {
+        int k = 0;
+        for (; k + 8 <= S; k += 8) {
+          f32x4 v[8];
+          float wk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            v[u] = *reinterpret_cast<const f32x4*>(op + (k + u) * sstride + c0);
+            wk[u] = lp[(int64_t)(k + u) * a.n_q];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o += __expf(wk[u] - M) * v[u];
+        }
+        for (; k < S; ++k) o += __expf(lp[(int64_t)k * a.n_q] - M) * *reinterpret_cast<const f32x4*>(op + k * sstride + c0);
+      } else {
+        for (int k = 0; k < S; ++k) {
+          const float wk = __expf(lp[(int64_t)k * a.n_q] - M);
+          for (int e = 0; c0 + e < R; ++e) o[e] += wk * op[k * sstride + c0 + e];
+        }
       }
-    } else {
-      for (int k = 0; k < S; ++k)
-        for (int e = 0; c0 + e < R; ++e) o[e] += wts[k] * op[k * sstride + c0 + e];
     }
     for (int e = 0; e < 4 && c0 + e < R; ++e) {
       const float v = any_nan ? NAN : o[e] * inv;
@@ -600,7 +611,7 @@ __global__ __launch_bounds__(128) void decode_merge(const DecodeArgs a) {
       else static_cast<float*>(a.out)[qrow * R + c0 + e] = v;
     }
   }
-  if (tid == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + logf(wsum));
+  if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
 }
 
 }  // namespace
@@ -631,9 +642,9 @@ hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t 
   const int grid = (groups > 0 ? groups : 1) * 8 * a.m_tiles;
   if (mfma) {
     if (a.d_rope == 64)
-      hipLaunchKernelGGL(decode_split_mfma<64>, dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(decode_split_mfma<64>, dim3(grid), dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(decode_split_mfma<0>, dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(decode_split_mfma<0>, dim3(grid), dim3(512), 0, stream, a);
   } else if (bf16) {
     hipLaunchKernelGGL(decode_split_generic<uint16_t>, dim3(grid), dim3(128), 0, stream, a);
   } else {
@@ -641,7 +652,9 @@ hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.batch == 0) return e;
-  hipLaunchKernelGGL(decode_merge, dim3((unsigned)((int64_t)a.batch * a.n_q)), dim3(128), 0, stream, a);
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  hipLaunchKernelGGL(decode_merge, dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)), dim3(64 * kMergeRows), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
