@@ -113,6 +113,9 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0, help="KV splits per request (0 = automatic)")
     ap.add_argument("--cpu-items", type=int, default=4096, help="oracle items for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after the timed region, copy this many MiB device-to-device 3 times (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -217,6 +220,15 @@ def main() -> int:
             torch.cuda.synchronize()
             stage[name] = sum(a.elapsed_time(b) for a, b in es) / len(es)
     stage["decode"] = dec_avg
+
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.copy_calibration_mb} MiB device-to-device")
 
     value = figs["bytes"] / (ms_step * 1e-3) / 1e9
     dec_gbs = figs["decode_bytes"] / (dec_avg * 1e-3) / 1e9

@@ -46,13 +46,28 @@ __device__ __forceinline__ uint32_t request_flags(int64_t L, int t_q, int max_bl
   return 0u;
 }
 
-// XCD-aware decode of the linear workgroup id: the m-tiles that share one
-// (request, range) -- and so read the same cache blocks -- get the same id
-// modulo 8, i.e. land on the same XCD and share its L2.
+// XCD-aware decode of the linear workgroup id (workgroup i runs on XCD i % 8,
+// each XCD with its own L2).  With a batch that is a multiple of 8, every
+// workgroup of request b -- all its ranges and query tiles -- lands on XCD
+// b % 8: the request's queries are fetched into one L2 only, and its split
+// partials are written to the L2 the merge of request b reads them from.
+// Otherwise the m-tiles that share one (request, range), and so read the same
+// cache blocks, land on the same XCD.
 __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int& b, int& s, int& mt, int& item) {
   const int lin = blockIdx.x;
   const int p_lo = lin & 7;
   const int rest = lin >> 3;
+  if (a.batch % 8 == 0) {
+    const int per_b = a.splits * a.m_tiles;
+    const int bg = rest / per_b;
+    const int r2 = rest - bg * per_b;
+    b = bg * 8 + p_lo;
+    s = r2 / a.m_tiles;
+    mt = r2 - s * a.m_tiles;
+    if (b >= a.batch) return false;
+    item = (b * a.splits + s) * a.m_tiles + mt;
+    return true;
+  }
   mt = rest % a.m_tiles;
   const int pair = (rest / a.m_tiles) * 8 + p_lo;
   if (pair >= a.n_pairs) return false;
@@ -555,9 +570,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Workgroups per request in the merge (kMergeRows query rows each).
+__device__ __host__ inline int merge_wg_per_request(int n_q) { return (n_q + kMergeRows - 1) / kMergeRows; }
+
 __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t qrow = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);  // b * n_q + q
+  int64_t qrow;  // b * n_q + q
+  if (a.batch % 8 == 0) {  // request b on XCD b % 8, where its partials were written
+    const int per_b = merge_wg_per_request(a.n_q);
+    const int rest = blockIdx.x >> 3;
+    const int bg = rest / per_b;
+    const int b_ = bg * 8 + (blockIdx.x & 7);
+    const int q_ = (rest - bg * per_b) * kMergeRows + (threadIdx.x >> 6);
+    if (q_ >= a.n_q) return;
+    qrow = (int64_t)b_ * a.n_q + q_;
+  } else {
+    qrow = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 6);
+  }
   if (qrow >= (int64_t)a.batch * a.n_q) return;
   const int b = (int)(qrow / a.n_q);
   const int q = (int)(qrow - (int64_t)b * a.n_q);
@@ -638,8 +667,13 @@ Plan decode_plan(int n_head, int kv_rank, int d_rope, int batch, int t_q, int ma
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t stream) {
-  const int groups = (a.n_pairs + 7) / 8;
-  const int grid = (groups > 0 ? groups : 1) * 8 * a.m_tiles;
+  int grid;
+  if (a.batch % 8 == 0 && a.batch > 0) {
+    grid = a.batch * a.splits * a.m_tiles;  // = (batch / 8) * 8 * splits * m_tiles
+  } else {
+    const int groups = (a.n_pairs + 7) / 8;
+    grid = (groups > 0 ? groups : 1) * 8 * a.m_tiles;
+  }
   if (mfma) {
     if (a.d_rope == 64)
       hipLaunchKernelGGL(decode_split_mfma<64>, dim3(grid), dim3(512), 0, stream, a);
@@ -653,8 +687,9 @@ hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.batch == 0) return e;
   const int64_t rows = (int64_t)a.batch * a.n_q;
-  hipLaunchKernelGGL(decode_merge, dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)), dim3(64 * kMergeRows), 0,
-                     stream, a);
+  const int64_t mgrid = a.batch % 8 == 0 ? (int64_t)a.batch * merge_wg_per_request(a.n_q)
+                                         : (rows + kMergeRows - 1) / kMergeRows;
+  hipLaunchKernelGGL(decode_merge, dim3((unsigned)mgrid), dim3(64 * kMergeRows), 0, stream, a);
   return hipGetLastError();
 }
 

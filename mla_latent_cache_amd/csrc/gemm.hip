@@ -36,6 +36,25 @@ __device__ __forceinline__ bf16x8 load8(const float* p) {
 template <typename TO>
 __device__ __forceinline__ void store_c(TO* out, int64_t idx, float v) { Storage<TO>::store(out, idx, v); }
 
+// Four consecutive outputs at out[idx .. idx + 3] (idx a multiple of 4).
+__device__ __forceinline__ void store4(float* out, int64_t idx, f32x4 v) { *reinterpret_cast<f32x4*>(out + idx) = v; }
+__device__ __forceinline__ void store4(uint16_t* out, int64_t idx, f32x4 v) {
+  *reinterpret_cast<uint2*>(out + idx) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// Activation operands of one 16-token tile: lane (l16, g) holds the eight
+// contraction elements 32 t + 8 g .. + 7 of token m0 + l16, for every k-step t.
+// All loads of a tile are issued together, so a tile costs one memory latency.
+constexpr int kMaxK = 16;  // contraction length up to 512
+
+template <typename TI>
+__device__ __forceinline__ void load_tile(bf16x8 (&A)[kMaxK], const TI* base, int64_t row_stride, int64_t n_a,
+                                          int64_t n_tok, int ksteps, int g) {
+#pragma unroll
+  for (int t = 0; t < kMaxK; ++t)
+    A[t] = (t < ksteps && n_a < n_tok) ? load8(base + n_a * row_stride + 32 * t + 8 * g) : zero_bf16x8();
+}
+
 // ---------------------------------------------------------------------------
 // Absorb, bf16 in.  Grid (n_head, kv_rank / 64); 256 threads.  DN = d_nope (multiple of 32).
 // W_UK[h][0:DN][c0:c0+64] is staged in LDS with a 160-byte row pitch (40 dwords = 8 * odd).
@@ -51,46 +70,87 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
   const int h = blockIdx.x, c0 = blockIdx.y * kCols;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int D = kv_rank + R;
+  const int ksteps = DN / 32;
+  const uint16_t* qbase = q_nope + (int64_t)h * DN;  // token n at qbase + n * H * DN
+  const int64_t qstride = (int64_t)H * DN;
 
-  // Stage the weight slice: DN rows x 128 bytes, 16 bytes per thread per step.
+  // First token tile's activations, then the weight slice (DN rows x 128 bytes).
+  bf16x8 A[2][kMaxK];
+  load_tile(A[0], qbase, qstride, l16, n_tok, ksteps, g);
+  if (n_tok > 16) load_tile(A[1], qbase, qstride, 16 + l16, n_tok, ksteps, g);
+
+  // The rope tail q_abs[n][h][kv_rank:] = q_pe[n][h] is copied by the first
+  // column slice, eight elements per thread and step.
+  if (blockIdx.y == 0) {
+    const int r8 = R / 8;
+    if (R % 8 == 0) {
+      for (int64_t idx = tid; idx < n_tok * r8; idx += 256) {
+        const int64_t n = idx / r8;
+        const int r = (int)(idx - n * r8) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(q_pe + (n * H + h) * R + r);
+        TO* dst = q_abs + (n * H + h) * D + kv_rank + r;
+        if constexpr (sizeof(TO) == 2) {
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          const bf16x8 b = as_bf16x8(v);
+          *reinterpret_cast<f32x4*>(dst) = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{(float)b[4], (float)b[5], (float)b[6], (float)b[7]};
+        }
+      }
+    } else {
+      for (int64_t idx = tid; idx < n_tok * R; idx += 256) {
+        const int64_t n = idx / R;
+        const int r = (int)(idx - n * R);
+        store_c(q_abs, (n * H + h) * D + kv_rank + r, bf16_to_f32(q_pe[(n * H + h) * R + r]));
+      }
+    }
+  }
+  // Thread tid stages 16 bytes of rows p = tid / 8 + 32 i (i < DN / 32): all
+  // loads are issued before the first LDS write.
   const uint16_t* wsrc = w_uk + (int64_t)h * DN * kv_rank + c0;
-  for (int idx = tid; idx < DN * 8; idx += 256) {
-    const int p = idx >> 3, c = (idx & 7) * 8;
-    *reinterpret_cast<u32x4*>(wl + p * PITCH + c) = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)p * kv_rank + c);
+  {
+    const int pr = tid >> 3, c = (tid & 7) * 8;
+    u32x4 st[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i)
+      if (i < ksteps) st[i] = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)(pr + 32 * i) * kv_rank + c);
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i)
+      if (i < ksteps) *reinterpret_cast<u32x4*>(wl + (pr + 32 * i) * PITCH + c) = st[i];
   }
   __syncthreads();
 
-  // The rope tail is copied once per (token, head) by the first column slice.
-  if (blockIdx.y == 0) {
-    for (int64_t idx = tid; idx < n_tok * R; idx += 256) {
-      const int64_t n = idx / R;
-      const int r = (int)(idx - n * R);
-      store_c(q_abs, (n * H + h) * D + kv_rank + r, bf16_to_f32(q_pe[(n * H + h) * R + r]));
-    }
-  }
-
-  // This wave's 16 columns; B operand rows (p) read transposed from LDS.
+  // This wave's 16 columns as the A operand of q_abs^T = W_UK^T q_nope^T
+  // (rows p read transposed from LDS); tokens are the N dimension, so each
+  // lane ends with four consecutive columns of one token.
   const int cw = w * 16;
-  const int ksteps = DN / 32;
-  for (int64_t m0 = 0; m0 < n_tok; m0 += 16) {
-    const int64_t n_a = m0 + l16;  // A-operand token of this lane
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int t = 0; t < ksteps; ++t) {
-      const bf16x8 A = n_a < n_tok ? load8(q_nope + (n_a * H + h) * DN + 32 * t + 8 * g) : zero_bf16x8();
-      // rows p0 .. p0+3 and p0+4 .. p0+7 at columns cw .. cw+15
-      const int p0 = 32 * t + 8 * g;
-      const int prow = p0 + (l16 >> 2);
+  bf16x8 B[kMaxK];
+#pragma unroll
+  for (int t = 0; t < kMaxK; ++t) {
+    if (t < ksteps) {
+      const int prow = 32 * t + 8 * g + (l16 >> 2);
       const int col = cw + 4 * (l16 & 3);
       const s16x4 b0 = lds_read_tr16(wl + prow * PITCH + col);
       const s16x4 b1 = lds_read_tr16(wl + (prow + 4) * PITCH + col);
-      const bf16x8 B = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc = mfma16x16x32(A, B, acc);
+      B[t] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      B[t] = zero_bf16x8();
     }
+  }
+  // Token tiles in pairs, so the two operand buffers are named statically;
+  // a buffer is refilled two tiles ahead once its MFMAs are issued.
+  auto tile = [&](int64_t m0, bf16x8 (&Ac)[kMaxK]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t n = m0 + 4 * g + i;
-      if (n < n_tok) store_c(q_abs, (n * H + h) * D + c0 + cw + l16, acc[i]);
-    }
+    for (int t = 0; t < kMaxK; ++t)
+      if (t < ksteps) acc = mfma16x16x32(B[t], Ac[t], acc);
+    if (m0 + 32 < n_tok) load_tile(Ac, qbase, qstride, m0 + 32 + l16, n_tok, ksteps, g);
+    const int64_t n = m0 + l16;
+    if (n < n_tok) store4(q_abs, (n * H + h) * D + c0 + cw + 4 * g, acc);
+  };
+  for (int64_t m0 = 0; m0 < n_tok; m0 += 32) {
+    tile(m0, A[0]);
+    if (m0 + 16 < n_tok) tile(m0 + 16, A[1]);
   }
 }
 
@@ -103,32 +163,35 @@ __global__ __launch_bounds__(256) void decompress_mfma(int H, int DV, int KR, in
                                                        const TI* __restrict__ o_lat,
                                                        const uint16_t* __restrict__ w_uv,
                                                        TO* __restrict__ out) {
-  constexpr int MAXK = 16;  // up to 512 / 32 contraction steps
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int j_b = blockIdx.y * kCols + w * 16 + l16;  // B-operand column (output index) of this lane
   const int ksteps = KR / 32;
-  bf16x8 Bk[MAXK];
+  const TI* obase = o_lat + (int64_t)h * KR;  // token n at obase + n * H * KR
+  const int64_t ostride = (int64_t)H * KR;
+  bf16x8 A[2][kMaxK];
+  load_tile(A[0], obase, ostride, l16, n_tok, ksteps, g);
+  if (n_tok > 16) load_tile(A[1], obase, ostride, 16 + l16, n_tok, ksteps, g);
+  bf16x8 Bk[kMaxK];
   const uint16_t* wrow = w_uv + ((int64_t)h * DV + j_b) * KR + 8 * g;
 #pragma unroll
-  for (int t = 0; t < MAXK; ++t)
+  for (int t = 0; t < kMaxK; ++t)
     Bk[t] = (t < ksteps && j_b < DV) ? load8(wrow + 32 * t) : zero_bf16x8();
-  const int jc = blockIdx.y * kCols + w * 16 + l16;  // C-operand column
-  for (int64_t m0 = 0; m0 < n_tok; m0 += 16) {
-    const int64_t n_a = m0 + l16;
+  // out^T = W_UV o_lat^T: weight rows are the M dimension, tokens N, so each
+  // lane ends with output columns j4 .. j4 + 3 of one token.
+  const int j4 = blockIdx.y * kCols + w * 16 + 4 * g;
+  auto tile = [&](int64_t m0, bf16x8 (&Ac)[kMaxK]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < MAXK; ++t) {
-      if (t < ksteps) {
-        const bf16x8 A = n_a < n_tok ? load8(o_lat + (n_a * H + h) * KR + 32 * t + 8 * g) : zero_bf16x8();
-        acc = mfma16x16x32(A, Bk[t], acc);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t n = m0 + 4 * g + i;
-      if (n < n_tok && jc < DV) store_c(out, (n * H + h) * DV + jc, acc[i]);
-    }
+    for (int t = 0; t < kMaxK; ++t)
+      if (t < ksteps) acc = mfma16x16x32(Bk[t], Ac[t], acc);
+    if (m0 + 32 < n_tok) load_tile(Ac, obase, ostride, m0 + 32 + l16, n_tok, ksteps, g);
+    const int64_t n = m0 + l16;
+    if (n < n_tok && j4 < DV) store4(out, (n * H + h) * DV + j4, acc);
+  };
+  for (int64_t m0 = 0; m0 < n_tok; m0 += 32) {
+    tile(m0, A[0]);
+    if (m0 + 16 < n_tok) tile(m0 + 16, A[1]);
   }
 }
 
@@ -183,7 +246,8 @@ unsigned generic_grid(int64_t total) {
 hipError_t launch_absorb(int H, int DN, int R, int KR, int64_t n_tok, const void* q_nope, const void* q_pe,
                          const void* w_uk, bool in_bf16, void* q_abs, bool out_bf16, hipStream_t stream) {
   if (n_tok == 0) return hipSuccess;
-  const bool mfma = in_bf16 && DN % 32 == 0 && KR % kCols == 0 && DN <= 512;
+  // (Four-column output stores need rows of a multiple of 4 elements.)
+  const bool mfma = in_bf16 && DN % 32 == 0 && KR % kCols == 0 && DN <= 512 && R % 4 == 0;
   if (mfma) {
     const dim3 grid(H, KR / kCols);
     const size_t lds = (size_t)DN * 80 * 2;
@@ -223,7 +287,7 @@ hipError_t launch_absorb(int H, int DN, int R, int KR, int64_t n_tok, const void
 hipError_t launch_decompress(int H, int DV, int KR, int64_t n_tok, const void* o_lat, bool o_bf16,
                              const void* w_uv, bool w_bf16, void* out, bool out_bf16, hipStream_t stream) {
   if (n_tok == 0) return hipSuccess;
-  const bool mfma = w_bf16 && KR % 32 == 0 && KR <= 512;
+  const bool mfma = w_bf16 && KR % 32 == 0 && KR <= 512 && DV % 4 == 0;
   if (mfma) {
     const dim3 grid(H, (DV + kCols - 1) / kCols);
     const uint16_t* wv = static_cast<const uint16_t*>(w_uv);
