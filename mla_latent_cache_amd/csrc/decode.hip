@@ -454,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(o + 16 * ct) = bad ? nan4 : acc[ct][n] * inv;
       }
-    } else {
+    } else if (n_tiles > 0 || bad) {  // an empty range leaves its partial unwritten (lse -inf: merge skips it)
       const int64_t prow = ((int64_t)b * a.splits + s) * a.n_q + q_row[n];
       float* o = a.o_part + prow * T::KV + col0;
 #pragma unroll
@@ -614,22 +614,35 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
       if (R - c0 >= 4) {
+        // Splits with lse -inf (empty ranges) contribute nothing and their
+        // partials may be unwritten: the loads (always inside the workspace)
+        // are issued regardless, and their values discarded by a select.
         int k = 0;
         for (; k + 8 <= S; k += 8) {
           f32x4 v[8];
           float wk[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            v[u] = *reinterpret_cast<const f32x4*>(op + (k + u) * sstride + c0);
             wk[u] = lp[(int64_t)(k + u) * a.n_q];
+            v[u] = *reinterpret_cast<const f32x4*>(op + (k + u) * sstride + c0);
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) o += __expf(wk[u] - M) * v[u];
+          for (int u = 0; u < 8; ++u) {
+            const bool live = wk[u] != -INFINITY;
+            const float wgt = live ? __expf(wk[u] - M) : 0.f;
+            const f32x4 vv = live ? v[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+            o += wgt * vv;
+          }
         }
-        for (; k < S; ++k) o += __expf(lp[(int64_t)k * a.n_q] - M) * *reinterpret_cast<const f32x4*>(op + k * sstride + c0);
+        for (; k < S; ++k) {
+          const float wk = lp[(int64_t)k * a.n_q];
+          if (wk != -INFINITY) o += __expf(wk - M) * *reinterpret_cast<const f32x4*>(op + k * sstride + c0);
+        }
       } else {
         for (int k = 0; k < S; ++k) {
-          const float wk = __expf(lp[(int64_t)k * a.n_q] - M);
+          const float lk = lp[(int64_t)k * a.n_q];
+          if (lk == -INFINITY) continue;
+          const float wk = __expf(lk - M);
           for (int e = 0; c0 + e < R; ++e) o[e] += wk * op[k * sstride + c0 + e];
         }
       }
@@ -641,6 +654,104 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs
     }
   }
   if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
+}
+
+// ---------------------------------------------------------------------------
+// Merge for many splits per request (few query rows, long requests): one
+// workgroup of kWideWaves waves per query row.  Wave v sums the contiguous
+// splits [v S / W, (v + 1) S / W); the per-wave sums are then added in wave
+// order through LDS, so the result does not depend on timing.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 16;
+constexpr int kWideMinSplits = 64;  // decode_merge_wide from this many splits on
+
+__global__ __launch_bounds__(64 * kWideWaves) void decode_merge_wide(const DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float wsum_lds[];  // [kWideWaves][kv_rank], then scratch
+  float* red = wsum_lds + kWideWaves * a.kv_rank;                  // [kWideWaves] reductions
+  const int tid = threadIdx.x, lane = tid & 63, v = tid >> 6;
+  int64_t qrow;
+  if (a.batch % 8 == 0) {  // request b on XCD b % 8, as in decode_merge
+    const int rest = blockIdx.x >> 3;
+    const int bg = rest / a.n_q;
+    qrow = (int64_t)(bg * 8 + (blockIdx.x & 7)) * a.n_q + (rest - bg * a.n_q);
+  } else {
+    qrow = blockIdx.x;
+  }
+  const int b = (int)(qrow / a.n_q);
+  const int q = (int)(qrow - (int64_t)b * a.n_q);
+  const int S = a.splits, R = a.kv_rank;
+  const float* lp = a.lse_part + (int64_t)b * S * a.n_q + q;
+
+  float mx = -INFINITY;
+  bool nan_seen = false;
+  for (int k = tid; k < S; k += 64 * kWideWaves) {
+    const float x = lp[(int64_t)k * a.n_q];
+    nan_seen |= isnan(x);
+    mx = fmaxf(mx, x);
+  }
+  mx = wave_max(mx);
+  const int any_nan = __syncthreads_or(nan_seen ? 1 : 0);
+  if (lane == 0) red[v] = mx;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int i = 0; i < kWideWaves; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+  float wpart = 0.f;
+  if (M != -INFINITY)
+    for (int k = tid; k < S; k += 64 * kWideWaves) wpart += __expf(lp[(int64_t)k * a.n_q] - M);
+  wpart = wave_sum(wpart);
+  if (lane == 0) red[v] = wpart;
+  __syncthreads();
+  float wsum = 0.f;
+  for (int i = 0; i < kWideWaves; ++i) wsum += red[i];
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+
+  const int k0 = (int)((int64_t)S * v / kWideWaves), k1 = (int)((int64_t)S * (v + 1) / kWideWaves);
+  const float* op = a.o_part + ((int64_t)b * S * a.n_q + q) * R;
+  const int64_t sstride = (int64_t)a.n_q * R;
+  for (int c0 = 4 * lane; c0 < R; c0 += 256) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      if (R - c0 >= 4) {
+        int k = k0;
+        for (; k + 4 <= k1; k += 4) {
+          f32x4 x[4];
+          float wk[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            wk[u] = lp[(int64_t)(k + u) * a.n_q];
+            x[u] = *reinterpret_cast<const f32x4*>(op + (k + u) * sstride + c0);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const bool live = wk[u] != -INFINITY;
+            o += (live ? __expf(wk[u] - M) : 0.f) * (live ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+        }
+        for (; k < k1; ++k) {
+          const float wk = lp[(int64_t)k * a.n_q];
+          if (wk != -INFINITY) o += __expf(wk - M) * *reinterpret_cast<const f32x4*>(op + k * sstride + c0);
+        }
+      } else {
+        for (int k = k0; k < k1; ++k) {
+          const float lk = lp[(int64_t)k * a.n_q];
+          if (lk == -INFINITY) continue;
+          const float wk = __expf(lk - M);
+          for (int e = 0; c0 + e < R; ++e) o[e] += wk * op[k * sstride + c0 + e];
+        }
+      }
+    }
+    for (int e = 0; e < 4 && c0 + e < R; ++e) wsum_lds[v * R + c0 + e] = o[e];
+  }
+  __syncthreads();
+  for (int c = tid; c < R; c += 64 * kWideWaves) {
+    float acc = 0.f;
+    for (int i = 0; i < kWideWaves; ++i) acc += wsum_lds[i * R + c];
+    const float val = any_nan ? NAN : acc * inv;
+    if (a.out_bf16) static_cast<uint16_t*>(a.out)[qrow * R + c] = f32_to_bf16(val);
+    else static_cast<float*>(a.out)[qrow * R + c] = val;
+  }
+  if (tid == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
 }
 
 }  // namespace
@@ -687,6 +798,11 @@ hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.batch == 0) return e;
   const int64_t rows = (int64_t)a.batch * a.n_q;
+  if (a.splits >= kWideMinSplits) {
+    const size_t lds = ((size_t)kWideWaves * a.kv_rank + kWideWaves) * sizeof(float);
+    hipLaunchKernelGGL(decode_merge_wide, dim3((unsigned)rows), dim3(64 * kWideWaves), lds, stream, a);
+    return hipGetLastError();
+  }
   const int64_t mgrid = a.batch % 8 == 0 ? (int64_t)a.batch * merge_wg_per_request(a.n_q)
                                          : (rows + kMergeRows - 1) / kMergeRows;
   hipLaunchKernelGGL(decode_merge, dim3((unsigned)mgrid), dim3(64 * kMergeRows), 0, stream, a);

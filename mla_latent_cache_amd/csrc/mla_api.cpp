@@ -38,14 +38,19 @@ mla_status check_decode_dims(const mla_dims* d) {
 // Automatic split count: enough (request, range, query tile) workgroups to give
 // every compute unit one (the MFMA kernel's LDS use allows one workgroup per
 // compute unit, and every extra split adds a partial to write and merge), or
-// two per compute unit for the small generic workgroups; no range shorter than
-// 8 cache blocks.
+// two per compute unit for the small generic workgroups; ranges of at most
+// kMaxRangeBlocks cache blocks, so that with ragged lengths no single
+// workgroup owns a whole long request; no range shorter than 8 cache blocks.
+constexpr int kMaxRangeBlocks = 256;
+
 int auto_splits(int n_head, int batch, int t_q, int max_blocks, int cus, bool mfma) {
   const int n_q = t_q * n_head;
   const int m_tiles = mfma ? (n_q + mla::kQRowsPerWG - 1) / mla::kQRowsPerWG : n_q;
   const long base = (long)(batch > 0 ? batch : 1) * m_tiles;
   const long target = mfma ? (long)cus : 2L * cus;
   long want = (target + base - 1) / base;
+  const long by_length = (max_blocks + kMaxRangeBlocks - 1) / kMaxRangeBlocks;
+  if (want < by_length) want = by_length;
   const long cap = (max_blocks + 7) / 8;
   if (want > cap) want = cap;
   if (want < 1) want = 1;

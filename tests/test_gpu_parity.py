@@ -102,6 +102,20 @@ def test_boundary_lengths_and_empty_requests():
         full_compare(case, res)
 
 
+@pytest.mark.parametrize("num_splits", [64, 128])
+def test_many_splits_wide_merge(num_splits):
+    # 64 or more splits per request take the wide merge (a workgroup per query
+    # row); a batch of 8 also takes the request-per-XCD mapping, and the empty
+    # request and the short ones leave most of their ranges empty.
+    lens = (1500, 0, 333, 17, 900, 64, 1, 2000)
+    spec = spec_small("nope_many_splits", "nope_long", batch=len(lens), fixed_lens=lens, max_blocks=128)
+    case = mi.make_case(spec)
+    res = run(DeviceCase(case), num_splits=num_splits)
+    assert res["status"] == 0
+    assert np.all(to_host(res["o_lat"])[1] == 0.0) and np.all(np.isneginf(to_host(res["lse"])[1]))
+    full_compare(case, res)
+
+
 # --------------------------------------------------------------------------
 # Full-size workloads, launch configuration of the benchmark, sampled outputs
 # --------------------------------------------------------------------------
