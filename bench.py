@@ -34,6 +34,40 @@ METRIC = "decode GB/s & TFLOP/s (% HBM/MFMA roofline); tokens·heads/s vs CPU or
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
+# Measured HBM traffic of one decode call (FETCH_SIZE and WRITE_SIZE counter
+# runs, calibrated against a device copy of known size) lives in a profile
+# summary, tagged with a hash of the sources it was measured on; it is reported
+# only while those sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_glm52_hbm_traffic.md")
+KERNEL_SOURCES = ["mla_latent_cache_amd/csrc/decode.hip", "mla_latent_cache_amd/csrc/device_common.hpp",
+                  "mla_latent_cache_amd/csrc/kernels.hpp", "mla_latent_cache_amd/csrc/mla_api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Bytes per decode call from the committed counter summary, or None when
+    there is none for this workload or the kernel sources changed since."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"<!-- traffic: (\{.*?\}) -->", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(rec["bytes_per_call"])
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -263,7 +297,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(spec.name),
             "algorithmic_bytes_per_launch": figs["decode_bytes"],
             "avg_launch_us": round(dec_avg * 1e3, 2),
             "mfma_tflops": round(dec_tflops, 2),
