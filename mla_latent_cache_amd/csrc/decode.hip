@@ -33,6 +33,7 @@
 #include "kernels.hpp"
 
 #include <math.h>
+#include <utility>
 
 namespace mla {
 namespace {
@@ -105,6 +106,25 @@ __device__ __forceinline__ void barrier_keep_loads() {
 }
 
 constexpr float kSlack = 8.f;   // log2 headroom before the softmax reference moves
+
+// Two 8-byte LDS reads at lds_addr + OFF and + OFF + 32, as separate
+// ds_read_b64 instructions (the compiler would pair them into one
+// ds_read2_b64, which this access pattern serves markedly slower).  The
+// results are not ready until a matching lgkm_wait.
+template <int OFF>
+__device__ __forceinline__ void lds_read_b64x2(uint32_t lds_addr, uint2& lo, uint2& hi) {
+  asm volatile("ds_read_b64 %0, %2 offset:%3\n\tds_read_b64 %1, %2 offset:%4"
+               : "=v"(lo), "=v"(hi)
+               : "v"(lds_addr), "i"(OFF), "i"(OFF + 32)
+               : "memory");
+}
+// Wait until at most N (< 16) of this wave's LDS operations are outstanding;
+// the two registers are tied to the wait so their uses cannot move above it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(uint2& a, uint2& b) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N) : "memory");
+}
 
 // ---------------------------------------------------------------------------
 // MFMA split kernel: bf16 queries and cache, kv_rank 512, rope width D_ROPE.
@@ -289,25 +309,41 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     }
   };
 
-  // Partial S^T of tile image `img` over this wave's k-steps, to xs[w].
+  // Partial S^T of tile image `img` over this wave's k-steps, to xs[w].  The
+  // K reads run kAhead (k-step, block) pairs ahead of the MFMAs, so at most
+  // 2 kAhead reads are outstanding and every wait count is exact.  (A fifth
+  // k-step that this wave does not own reads padding and neighbouring-row
+  // columns inside the tile image, all finite, and is not used.)
   auto s_part = [&](const u32x4* img) {
+    constexpr int NP = 2 * KQ;  // (k-step, block) pairs
+    constexpr int kAhead = 7;
+    static_assert(NP > kAhead && 2 * kAhead < 16, "read-ahead must fit the LDS counter");
+    const uint32_t ka = lds_addr(reinterpret_cast<const char*>(img) + k_off);
+    uint2 kr[KQ][2][2];
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (lds_read_b64x2<(I % 2) * T::BLK_IMG * 16 + 256 * (I / 2)>(ka, kr[I / 2][I % 2][0], kr[I / 2][I % 2][1]), ...);
+    }(std::make_integer_sequence<int, kAhead>{});
     f32x4 sp[2][2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) sp[rt][0] = sp[rt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const char* kb = reinterpret_cast<const char*>(img) + k_off;
-#pragma unroll
-    for (int j = 0; j < KQ; ++j) {
-      if (j < 4 || j < nk) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(kb + rt * T::BLK_IMG * 16 + 256 * j);
-          const uint2 hi = *reinterpret_cast<const uint2*>(kb + rt * T::BLK_IMG * 16 + 256 * j + 32);
-          const bf16x8 kA = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
-          sp[rt][0] = mfma16x16x32(kA, qf[0][j], sp[rt][0]);
-          sp[rt][1] = mfma16x16x32(kA, qf[1][j], sp[rt][1]);
-        }
-      }
-    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (([&] {
+         constexpr int j = I / 2, rt = I % 2;
+         // pairs issued so far: min(I + kAhead, NP); those after pair I are outstanding
+         constexpr int issued = I + kAhead < NP ? I + kAhead : NP;
+         lgkm_wait<2 * (issued - 1 - I)>(kr[j][rt][0], kr[j][rt][1]);
+         if (j < 4 || j < nk) {
+           const bf16x8 kA = as_bf16x8(u32x4{kr[j][rt][0].x, kr[j][rt][0].y, kr[j][rt][1].x, kr[j][rt][1].y});
+           sp[rt][0] = mfma16x16x32(kA, qf[0][j], sp[rt][0]);
+           sp[rt][1] = mfma16x16x32(kA, qf[1][j], sp[rt][1]);
+         }
+         if constexpr (I + kAhead < NP) {
+           constexpr int P = I + kAhead;
+           lds_read_b64x2<(P % 2) * T::BLK_IMG * 16 + 256 * (P / 2)>(ka, kr[P / 2][P % 2][0], kr[P / 2][P % 2][1]);
+         }
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, NP>{});
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -560,6 +596,7 @@ __global__ __launch_bounds__(128) void decode_split_generic(const DecodeArgs a) 
 // so each lane has up to sixteen 16-byte partial loads in flight.
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 4;
+constexpr int kMergeRegSplits = 16;  // register-resident merge up to this many splits
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -592,6 +629,56 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs
   const int q = (int)(qrow - (int64_t)b * a.n_q);
   const int S = a.splits, R = a.kv_rank;
   const float* lp = a.lse_part + (int64_t)b * S * a.n_q + q;  // split k at lp[k * n_q]
+  const float* op = a.o_part + ((int64_t)b * S * a.n_q + q) * R;
+  const int64_t sstride = (int64_t)a.n_q * R;
+
+  if (R == 2 * 256 && S <= kMergeRegSplits) {
+    // Every LSE and partial vector of the row is loaded at once (one memory
+    // latency); lane l owns columns 4 l .. + 3 and 256 + 4 l .. + 3.  Loads past
+    // the last split repeat it and are masked out.
+    float lk[kMergeRegSplits];
+    f32x4 v0[kMergeRegSplits], v1[kMergeRegSplits];
+#pragma unroll
+    for (int k = 0; k < kMergeRegSplits; ++k) {
+      const int kk = k < S ? k : S - 1;
+      lk[k] = lp[(int64_t)kk * a.n_q];
+      v0[k] = *reinterpret_cast<const f32x4*>(op + kk * sstride + 4 * lane);
+      v1[k] = *reinterpret_cast<const f32x4*>(op + kk * sstride + 256 + 4 * lane);
+    }
+    float M = -INFINITY;
+    bool any_nan = false;
+#pragma unroll
+    for (int k = 0; k < kMergeRegSplits; ++k) {
+      if (k < S) {
+        any_nan |= isnan(lk[k]);
+        M = fmaxf(M, lk[k]);
+      }
+    }
+    float wsum = 0.f;
+    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+#pragma unroll
+    for (int k = 0; k < kMergeRegSplits; ++k) {
+      const bool live = k < S && lk[k] != -INFINITY && M != -INFINITY;  // empty splits may be unwritten
+      const float wk = live ? __expf(lk[k] - M) : 0.f;
+      wsum += wk;
+      o0 += wk * (live ? v0[k] : f32x4{0.f, 0.f, 0.f, 0.f});
+      o1 += wk * (live ? v1[k] : f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+    const f32x4 r0 = any_nan ? nan4 : o0 * inv, r1 = any_nan ? nan4 : o1 * inv;
+    if (a.out_bf16) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * R;
+      *reinterpret_cast<uint2*>(o + 4 * lane) = uint2{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3])};
+      *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = uint2{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+    } else {
+      float* o = static_cast<float*>(a.out) + qrow * R;
+      *reinterpret_cast<f32x4*>(o + 4 * lane) = r0;
+      *reinterpret_cast<f32x4*>(o + 256 + 4 * lane) = r1;
+    }
+    if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
+    return;
+  }
 
   float mx = -INFINITY;
   bool nan_seen = false;
@@ -608,8 +695,6 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs
   const float wsum = wave_sum(wpart);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
-  const float* op = a.o_part + ((int64_t)b * S * a.n_q + q) * R;
-  const int64_t sstride = (int64_t)a.n_q * R;
   for (int c0 = 4 * lane; c0 < R; c0 += 256) {
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
