@@ -8,8 +8,10 @@ d_v 256, kv_rank 512; 32 requests x 4096 cached rows; 16-row blocks; bf16).
 
 Consecutive steps cycle through --copies independent copies of every input
 (cache, block table, queries, weights), so the 256 MB Infinity Cache cannot
-serve a step from the previous one.  HIP events on the launch stream time
-each stage live inside the timed region.  The CPU baseline runs the oracle
+serve a step from the previous one.  The timed region replays one HIP graph
+per input copy holding the step's four kernels (--eager launches them from
+the host instead); the decode call's own duration for the roofline comes
+from HIP events on its stream around each call.  The CPU baseline runs the oracle
 (absorbed form: absorb, two-pass attention, decompress) over the same
 workload on the host cores.
 
@@ -147,6 +149,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0, help="KV splits per request (0 = automatic)")
     ap.add_argument("--cpu-items", type=int, default=4096, help="oracle items for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel of a timed step from the host instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after the timed region, copy this many MiB device-to-device 3 times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -199,9 +203,8 @@ def main() -> int:
     splits = mla.mla_decode_resolve_splits(dims, B, T, spec.max_blocks, args.num_splits)
     ws = torch.empty(mla.mla_decode_workspace_size(dims, B, T, spec.max_blocks, 16, args.num_splits),
                      dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-
     def step(c, ev=None):
+        stream = torch.cuda.current_stream()
         if not spec.q_given:
             mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
         if ev is not None:
@@ -222,21 +225,46 @@ def main() -> int:
         log(f"device data-error flags {status:#x}")
         return 1
 
-    # Timed region: the whole step, and the decode call alone on the same stream.
-    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # The step's four kernels (absorb, split, merge, decompress) are captured in
+    # one HIP graph per input copy, as a serving loop would launch them; the
+    # timed region replays them.  --eager launches every kernel from the host.
+    stream = torch.cuda.current_stream()
+    graphs = []
+    if not args.eager:
+        cap = torch.cuda.Stream()
+        for c in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(c)
+            graphs.append(g)
+        for k in range(max(1, args.warmup)):
+            graphs[k % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+    # Timed region: the whole step.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for k in range(args.steps):
-        step(copies[k % len(copies)], ev_dec[k])
+        if graphs:
+            graphs[k % len(graphs)].replay()
+        else:
+            step(copies[k % len(copies)])
     t1.record(stream)
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
+
+    # The decode call alone: HIP events on its stream around each call.
+    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(copies[k % len(copies)], ev_dec[k])
+    torch.cuda.synchronize()
     dec_ms = sorted(a.elapsed_time(b) for a, b in ev_dec)
     dec_avg = sum(dec_ms) / len(dec_ms)
-    log(f"{ms_step * 1e3:.1f} us/step; decode call avg {dec_avg * 1e3:.1f} us (min {dec_ms[0] * 1e3:.1f})")
+    log(f"{ms_step * 1e3:.1f} us/step ({'host launches' if args.eager else 'HIP graph replay'}); "
+        f"decode call avg {dec_avg * 1e3:.1f} us (min {dec_ms[0] * 1e3:.1f})")
 
     # Stage split (separate, untimed-for-value pass): absorb and decompress alone.
     stage = {}
@@ -289,6 +317,7 @@ def main() -> int:
         },
         "tflops": round(figs["flops"] / (ms_step * 1e-3) / 1e12, 3),
         "tokens_heads_per_s": round(figs["tokens_heads"] / (ms_step * 1e-3), 1),
+        "step_launch": "host launches" if args.eager else "HIP graph replay (absorb, split, merge, decompress)",
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "roofline": {
             "kernel": "decode call: decode_split_mfma + decode_merge",

@@ -116,6 +116,46 @@ def test_many_splits_wide_merge(num_splits):
     full_compare(case, res)
 
 
+def test_hip_graph_replay_matches_eager():
+    # The path captured in one HIP graph (absorb, split kernel, merge,
+    # decompress) and replayed three times, with eager launches on other
+    # inputs between the replays, reproduces the eager outputs bit for bit.
+    lens = (1, 17, 100, 300, 64, 0, 33, 200)
+    spec = spec_small("glm52_graph", "glm52_decode", batch=len(lens), fixed_lens=lens, max_blocks=20)
+    case = mi.make_case(spec)
+    dc = DeviceCase(case)
+    ref = run(dc, num_splits=3)
+    other = DeviceCase(mi.make_case(spec_small("glm52_graph_other", "glm52_decode", batch=2,
+                                               fixed_lens=(50, 7), max_blocks=4)))
+    dims = dims_tuple(spec)
+    B, H, D, R = spec.batch, spec.n_head, spec.D, spec.kv_rank
+    q_abs = torch.empty(B, 1, H, D, dtype=torch.bfloat16, device="cuda")
+    out_lat = torch.empty(B, 1, H, R, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, 1, H, dtype=torch.float32, device="cuda")
+    out = torch.empty(B, H, spec.d_v, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_size(dims, B, 1, dc.bt.shape[1], 16, 3), dtype=torch.uint8,
+                     device="cuda")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        st = torch.cuda.current_stream()
+        mla.mla_absorb_q(dims, dc.q_nope, dc.q_pe, dc.w_uk, q_abs, st)
+        mla.mla_decode_attention(dims, case.scale, q_abs, dc.kv, dc.bt, dc.sl, out_lat, lse, ws, 3, st)
+        mla.mla_decompress_v(dims, out_lat, dc.w_uv, out, st)
+    for rep in range(3):
+        for t in (q_abs, out_lat, out):
+            t.zero_()
+        lse.fill_(7.0)
+        g.replay()
+        run(other, num_splits=2)  # eager work between replays
+        torch.cuda.synchronize()
+        assert mla.mla_decode_status(ws) == 0
+        assert torch.equal(q_abs, ref["q_abs"]), rep
+        assert torch.equal(out_lat, ref["o_lat"]), rep
+        assert torch.equal(lse, ref["lse"]), rep
+        assert torch.equal(out, ref["out"]), rep
+
+
 # --------------------------------------------------------------------------
 # Full-size workloads, launch configuration of the benchmark, sampled outputs
 # --------------------------------------------------------------------------
