@@ -42,22 +42,49 @@ __device__ __forceinline__ void store4(uint16_t* out, int64_t idx, f32x4 v) {
   *reinterpret_cast<uint2*>(out + idx) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-// Activation operands of one 16-token tile: lane (l16, g) holds the eight
-// contraction elements 32 t + 8 g .. + 7 of token m0 + l16, for every k-step t.
-// All loads of a tile are issued together, so a tile costs one memory latency.
-constexpr int kMaxK = 16;  // contraction length up to 512
+constexpr int kMaxK = 16;   // contraction length up to 512 (32 per k-step)
+constexpr int kTC = 64;     // tokens staged in LDS at a time
+
+// Stage activations act[m0 + i][h][0:K] (i < kTC, rows past n_tok as zeros)
+// into LDS as bf16 rows of pitch K + 8 elements (16 bytes of padding: the
+// 16-byte operand reads of 16 consecutive rows then cover all 64 banks).
+// Every thread issues all of its global loads before its first LDS write.
+constexpr int kStagePer = kTC * 512 / 8 / 256;  // most 8-element chunks per thread (K <= 512)
 
 template <typename TI>
-__device__ __forceinline__ void load_tile(bf16x8 (&A)[kMaxK], const TI* base, int64_t row_stride, int64_t n_a,
-                                          int64_t n_tok, int ksteps, int g) {
+__device__ __forceinline__ void load_tokens(bf16x8 (&v)[kStagePer], const TI* act, int64_t row_stride, int64_t m0,
+                                            int64_t n_tok, int K, int tid) {
+  const int c8n = K / 8;  // 8-element chunks per row
 #pragma unroll
-  for (int t = 0; t < kMaxK; ++t)
-    A[t] = (t < ksteps && n_a < n_tok) ? load8(base + n_a * row_stride + 32 * t + 8 * g) : zero_bf16x8();
+  for (int i = 0; i < kStagePer; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx / c8n, c8 = idx - r * c8n;
+    v[i] = (r < kTC && m0 + r < n_tok) ? load8(act + (m0 + r) * row_stride + 8 * c8) : zero_bf16x8();
+  }
+}
+
+__device__ __forceinline__ void store_tokens(uint16_t* lds, const bf16x8 (&v)[kStagePer], int K, int tid) {
+  const int c8n = K / 8;
+#pragma unroll
+  for (int i = 0; i < kStagePer; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx / c8n, c8 = idx - r * c8n;
+    if (r < kTC) *reinterpret_cast<bf16x8*>(lds + r * (K + 8) + 8 * c8) = v[i];
+  }
+}
+
+// B operand (tokens as the N dimension) of k-step t for token row `row` of
+// the staged chunk: contraction elements 32 t + 8 g .. + 7.
+__device__ __forceinline__ bf16x8 token_operand(const uint16_t* lds, int row, int K, int t, int g) {
+  return *reinterpret_cast<const bf16x8*>(lds + row * (K + 8) + 32 * t + 8 * g);
 }
 
 // ---------------------------------------------------------------------------
 // Absorb, bf16 in.  Grid (n_head, kv_rank / 64); 256 threads.  DN = d_nope (multiple of 32).
-// W_UK[h][0:DN][c0:c0+64] is staged in LDS with a 160-byte row pitch (40 dwords = 8 * odd).
+// LDS: W_UK[h][0:DN][c0:c0+64] with a 160-byte row pitch (40 dwords = 8 * odd),
+// then kTC staged q_nope rows.  q_abs^T = W_UK^T q_nope^T: the weight columns
+// are the M dimension (read transposed from LDS), tokens the N dimension, so
+// each lane ends with four consecutive columns of one token.
 // ---------------------------------------------------------------------------
 template <typename TO>
 __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_rank, int64_t n_tok,
@@ -65,8 +92,9 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
                                                    const uint16_t* __restrict__ q_pe,
                                                    const uint16_t* __restrict__ w_uk,
                                                    TO* __restrict__ q_abs) {
-  constexpr int PITCH = 80;  // elements per LDS row (64 used)
-  extern __shared__ __attribute__((aligned(16))) uint16_t wl[];  // [DN][PITCH]
+  constexpr int PITCH = 80;  // elements per weight row in LDS (64 used)
+  extern __shared__ __attribute__((aligned(16))) uint16_t wl[];  // [DN][PITCH], then [kTC][DN + 8]
+  uint16_t* al = wl + DN * PITCH;
   const int h = blockIdx.x, c0 = blockIdx.y * kCols;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
   const int D = kv_rank + R;
@@ -74,10 +102,22 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
   const uint16_t* qbase = q_nope + (int64_t)h * DN;  // token n at qbase + n * H * DN
   const int64_t qstride = (int64_t)H * DN;
 
-  // First token tile's activations, then the weight slice (DN rows x 128 bytes).
-  bf16x8 A[2][kMaxK];
-  load_tile(A[0], qbase, qstride, l16, n_tok, ksteps, g);
-  if (n_tok > 16) load_tile(A[1], qbase, qstride, 16 + l16, n_tok, ksteps, g);
+  // Weight slice: thread tid stages 16 bytes of rows p = tid / 8 + 32 i; its
+  // loads go out together with the first token chunk's.
+  const uint16_t* wsrc = w_uk + (int64_t)h * DN * kv_rank + c0;
+  {
+    const int pr = tid >> 3, c = (tid & 7) * 8;
+    u32x4 st[kMaxK];
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i)
+      if (i < ksteps) st[i] = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)(pr + 32 * i) * kv_rank + c);
+    bf16x8 v[kStagePer];
+    load_tokens(v, qbase, qstride, 0, n_tok, DN, tid);
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i)
+      if (i < ksteps) *reinterpret_cast<u32x4*>(wl + (pr + 32 * i) * PITCH + c) = st[i];
+    store_tokens(al, v, DN, tid);
+  }
 
   // The rope tail q_abs[n][h][kv_rank:] = q_pe[n][h] is copied by the first
   // column slice, eight elements per thread and step.
@@ -105,24 +145,9 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
       }
     }
   }
-  // Thread tid stages 16 bytes of rows p = tid / 8 + 32 i (i < DN / 32): all
-  // loads are issued before the first LDS write.
-  const uint16_t* wsrc = w_uk + (int64_t)h * DN * kv_rank + c0;
-  {
-    const int pr = tid >> 3, c = (tid & 7) * 8;
-    u32x4 st[kMaxK];
-#pragma unroll
-    for (int i = 0; i < kMaxK; ++i)
-      if (i < ksteps) st[i] = *reinterpret_cast<const u32x4*>(wsrc + (int64_t)(pr + 32 * i) * kv_rank + c);
-#pragma unroll
-    for (int i = 0; i < kMaxK; ++i)
-      if (i < ksteps) *reinterpret_cast<u32x4*>(wl + (pr + 32 * i) * PITCH + c) = st[i];
-  }
   __syncthreads();
 
-  // This wave's 16 columns as the A operand of q_abs^T = W_UK^T q_nope^T
-  // (rows p read transposed from LDS); tokens are the N dimension, so each
-  // lane ends with four consecutive columns of one token.
+  // This wave's 16 weight columns as the A operand (rows p read transposed from LDS).
   const int cw = w * 16;
   bf16x8 B[kMaxK];
 #pragma unroll
@@ -137,61 +162,66 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
       B[t] = zero_bf16x8();
     }
   }
-  // Token tiles in pairs, so the two operand buffers are named statically;
-  // a buffer is refilled two tiles ahead once its MFMAs are issued.
-  auto tile = [&](int64_t m0, bf16x8 (&Ac)[kMaxK]) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t m0 = 0; m0 < n_tok; m0 += kTC) {
+    if (m0 > 0) {
+      __syncthreads();  // every wave is done with the previous chunk
+      bf16x8 v[kStagePer];
+      load_tokens(v, qbase, qstride, m0, n_tok, DN, tid);
+      store_tokens(al, v, DN, tid);
+      __syncthreads();
+    }
+    for (int s16 = 0; s16 < kTC && m0 + s16 < n_tok; s16 += 16) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < kMaxK; ++t)
-      if (t < ksteps) acc = mfma16x16x32(B[t], Ac[t], acc);
-    if (m0 + 32 < n_tok) load_tile(Ac, qbase, qstride, m0 + 32 + l16, n_tok, ksteps, g);
-    const int64_t n = m0 + l16;
-    if (n < n_tok) store4(q_abs, (n * H + h) * D + c0 + cw + 4 * g, acc);
-  };
-  for (int64_t m0 = 0; m0 < n_tok; m0 += 32) {
-    tile(m0, A[0]);
-    if (m0 + 16 < n_tok) tile(m0 + 16, A[1]);
+      for (int t = 0; t < kMaxK; ++t)
+        if (t < ksteps) acc = mfma16x16x32(B[t], token_operand(al, s16 + l16, DN, t, g), acc);
+      const int64_t n = m0 + s16 + l16;
+      if (n < n_tok) store4(q_abs, (n * H + h) * D + c0 + cw + 4 * g, acc);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Decompress, bf16 weights.  Grid (n_head, d_v / 64); 256 threads; kv_rank = KR
-// (multiple of 32, at most 512).  Each wave keeps its 16 weight rows in VGPRs.
+// (multiple of 32, at most 512).  Each wave keeps its 16 weight rows in VGPRs
+// (the A operand of out^T = W_UV o_lat^T); o_lat rows are staged in LDS kTC
+// tokens at a time and read as the N-dimension operand, so each lane ends with
+// output columns j4 .. j4 + 3 of one token.
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void decompress_mfma(int H, int DV, int KR, int64_t n_tok,
                                                        const TI* __restrict__ o_lat,
                                                        const uint16_t* __restrict__ w_uv,
                                                        TO* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t ol[];  // [kTC][KR + 8]
   const int h = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const int j_b = blockIdx.y * kCols + w * 16 + l16;  // B-operand column (output index) of this lane
+  const int j_b = blockIdx.y * kCols + w * 16 + l16;  // weight row (output index) of this lane's A operand
   const int ksteps = KR / 32;
   const TI* obase = o_lat + (int64_t)h * KR;  // token n at obase + n * H * KR
   const int64_t ostride = (int64_t)H * KR;
-  bf16x8 A[2][kMaxK];
-  load_tile(A[0], obase, ostride, l16, n_tok, ksteps, g);
-  if (n_tok > 16) load_tile(A[1], obase, ostride, 16 + l16, n_tok, ksteps, g);
   bf16x8 Bk[kMaxK];
   const uint16_t* wrow = w_uv + ((int64_t)h * DV + j_b) * KR + 8 * g;
 #pragma unroll
   for (int t = 0; t < kMaxK; ++t)
     Bk[t] = (t < ksteps && j_b < DV) ? load8(wrow + 32 * t) : zero_bf16x8();
-  // out^T = W_UV o_lat^T: weight rows are the M dimension, tokens N, so each
-  // lane ends with output columns j4 .. j4 + 3 of one token.
   const int j4 = blockIdx.y * kCols + w * 16 + 4 * g;
-  auto tile = [&](int64_t m0, bf16x8 (&Ac)[kMaxK]) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t m0 = 0; m0 < n_tok; m0 += kTC) {
+    if (m0 > 0) __syncthreads();  // every wave is done with the previous chunk
+    {
+      bf16x8 v[kStagePer];
+      load_tokens(v, obase, ostride, m0, n_tok, KR, tid);
+      store_tokens(ol, v, KR, tid);
+    }
+    __syncthreads();
+    for (int s16 = 0; s16 < kTC && m0 + s16 < n_tok; s16 += 16) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < kMaxK; ++t)
-      if (t < ksteps) acc = mfma16x16x32(Bk[t], Ac[t], acc);
-    if (m0 + 32 < n_tok) load_tile(Ac, obase, ostride, m0 + 32 + l16, n_tok, ksteps, g);
-    const int64_t n = m0 + l16;
-    if (n < n_tok && j4 < DV) store4(out, (n * H + h) * DV + j4, acc);
-  };
-  for (int64_t m0 = 0; m0 < n_tok; m0 += 32) {
-    tile(m0, A[0]);
-    if (m0 + 16 < n_tok) tile(m0 + 16, A[1]);
+      for (int t = 0; t < kMaxK; ++t)
+        if (t < ksteps) acc = mfma16x16x32(Bk[t], token_operand(ol, s16 + l16, KR, t, g), acc);
+      const int64_t n = m0 + s16 + l16;
+      if (n < n_tok && j4 < DV) store4(out, (n * H + h) * DV + j4, acc);
+    }
   }
 }
 
@@ -250,7 +280,7 @@ hipError_t launch_absorb(int H, int DN, int R, int KR, int64_t n_tok, const void
   const bool mfma = in_bf16 && DN % 32 == 0 && KR % kCols == 0 && DN <= 512 && R % 4 == 0;
   if (mfma) {
     const dim3 grid(H, KR / kCols);
-    const size_t lds = (size_t)DN * 80 * 2;
+    const size_t lds = (size_t)DN * 80 * 2 + (size_t)kTC * (DN + 8) * 2;
     const uint16_t *qn = static_cast<const uint16_t*>(q_nope), *qp = static_cast<const uint16_t*>(q_pe),
                    *wk = static_cast<const uint16_t*>(w_uk);
     if (out_bf16)
@@ -291,8 +321,9 @@ hipError_t launch_decompress(int H, int DV, int KR, int64_t n_tok, const void* o
   if (mfma) {
     const dim3 grid(H, (DV + kCols - 1) / kCols);
     const uint16_t* wv = static_cast<const uint16_t*>(w_uv);
+    const size_t lds = (size_t)kTC * (KR + 8) * 2;
 #define MLA_DECOMP(TI, TO)                                                                               \
-  hipLaunchKernelGGL((decompress_mfma<TI, TO>), grid, dim3(256), 0, stream, H, DV, KR, n_tok,              \
+  hipLaunchKernelGGL((decompress_mfma<TI, TO>), grid, dim3(256), lds, stream, H, DV, KR, n_tok,            \
                      static_cast<const TI*>(o_lat), wv, static_cast<TO*>(out))
     if (o_bf16 && out_bf16) MLA_DECOMP(uint16_t, uint16_t);
     else if (o_bf16) MLA_DECOMP(uint16_t, float);
