@@ -355,3 +355,81 @@ def sample_items(key_seed: int, batch: int, t_q: int, n_head: int, n: int,
         items.add((b * t_q + i) * n_head + h)
     flat = np.array(sorted(items), dtype=np.int64)
     return np.stack([flat // (t_q * n_head), (flat // n_head) % t_q, flat % n_head], axis=1).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Cache-append prolog inputs
+# --------------------------------------------------------------------------
+# GLM-5.2 rope_theta, the base of the pages' rope permutation test.
+ROPE_BASE = 8.0e6
+
+
+@dataclass
+class Append:
+    """New tokens of one step, before RmsNorm and rope.  Storage arrays are
+    float32 or bfloat16 bits (uint16), row-major."""
+    c_kv: np.ndarray        # [n_tok][kv_rank], before RmsNorm
+    k_pe: np.ndarray        # [n_tok][d_rope], before rope
+    q_pe: np.ndarray        # [n_tok][H][d_rope], before rope
+    gamma: np.ndarray       # [kv_rank]
+    positions: np.ndarray   # int32 [n_tok]
+    slots: np.ndarray       # int64 [n_tok] flat cache rows, -1 = padding token
+    eps: float = RMS_EPS
+    base: float = ROPE_BASE
+
+
+def append_values(spec: Spec, n_tok: int, tag: str = "append") -> tuple:
+    """(c_kv, k_pe, q_pe, gamma) of n_tok new tokens.  c_kv rows are
+    N(0, 1) times a per-token log-normal magnitude exp(0.5 N(0, 1)), so row
+    norms differ; gamma is 1 + 0.1 N(0, 1)."""
+    Lk, R, H = spec.kv_rank, spec.d_rope, spec.n_head
+    mag = np.exp(0.5 * normals(tensor_key(spec.seed, tag + ".mag"), 0, n_tok))
+    c = normals(tensor_key(spec.seed, tag + ".c_kv"), 0, n_tok * Lk).reshape(n_tok, Lk) * mag[:, None]
+    k = normals(tensor_key(spec.seed, tag + ".k_pe"), 0, n_tok * R).reshape(n_tok, R)
+    q = normals(tensor_key(spec.seed, tag + ".q_pe"), 0, n_tok * H * R).reshape(n_tok, H, R)
+    g = 1.0 + 0.1 * normals(tensor_key(spec.seed, tag + ".gamma"), 0, Lk)
+    vs = spec.value_scale
+    return (store(c * vs, spec.dtype), store(k * vs, spec.dtype), store(q * vs, spec.dtype),
+            store(g, spec.dtype))
+
+
+def step_append(spec: Spec, seq_lens, block_table, n_pad: int = 0, tag: str = "append") -> Append:
+    """The new tokens of one decode step, request-major (b, i).
+
+    seq_lens counts each request's rows including its t_q new ones, so query i
+    of request b is logical row p = L - t_q + i, stored at flat cache row
+    block_table[b][p // 16] * 16 + p % 16, with rope position p.  Requests
+    shorter than t_q get padding slots (-1).  n_pad padding tokens (slot -1,
+    position 0) follow, as when a batch is padded to a fixed size."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    B, T = lens.shape[0], spec.t_q
+    n_tok = B * T + n_pad
+    pos = np.zeros(n_tok, np.int32)
+    slots = np.full(n_tok, -1, np.int64)
+    for b in range(B):
+        L = int(lens[b])
+        if L < T:
+            continue
+        for i in range(T):
+            p = L - T + i
+            pos[b * T + i] = p
+            slots[b * T + i] = int(block_table[b, p // BLOCK_SIZE]) * BLOCK_SIZE + p % BLOCK_SIZE
+    c, k, q, g = append_values(spec, n_tok, tag)
+    return Append(c, k, q, g, pos, slots)
+
+
+def random_slots(key: int, num_slots: int, n_tok: int, n_skip: int = 0, n_out: int = 0) -> np.ndarray:
+    """n_tok slot entries: distinct valid rows of [0, num_slots), with n_skip
+    of them replaced by -1 and n_out by out-of-range rows (>= num_slots), at
+    random places."""
+    assert n_tok - n_skip - n_out <= num_slots
+    valid = np.argsort(draws(key, 0, num_slots), kind="stable")[:n_tok].astype(np.int64)
+    where = np.argsort(draws(key, num_slots, n_tok), kind="stable")
+    valid[where[:n_skip]] = -1
+    valid[where[n_skip:n_skip + n_out]] = num_slots + np.arange(n_out, dtype=np.int64) * 7
+    return valid
+
+
+def random_positions(key: int, n_tok: int, max_pos: int) -> np.ndarray:
+    """int32 positions uniform in [0, max_pos]."""
+    return np.floor(uniforms(key, 0, n_tok) * (max_pos + 1)).astype(np.int32)

@@ -54,6 +54,11 @@ def _load():
     lib.mla_oracle_rope_interleaved.argtypes = [vp, i32, dbl, dbl]
     lib.mla_oracle_rope_neox.argtypes = [vp, i32, dbl, dbl]
     lib.mla_oracle_norm_to_neox_perm.argtypes = [i32, vp]
+    lib.mla_oracle_rmsnorm.argtypes = [vp, i32, i64, i32, vp, i32, dbl, vp]
+    lib.mla_oracle_rope_rows.argtypes = [vp, i32, i64, i32, i32, vp, dbl, i32, vp]
+    lib.mla_oracle_cache_append.restype = i64
+    lib.mla_oracle_cache_append.argtypes = [i32, i32, i64, vp, vp, i32, vp, i32, dbl, vp, dbl,
+                                            i32, vp, vp, i64]
     _LIB = lib
     return lib
 
@@ -241,3 +246,59 @@ def norm_to_neox_perm(n_dims: int) -> np.ndarray:
     p = np.empty(n_dims, np.int32)
     _load().mla_oracle_norm_to_neox_perm(int(n_dims), _p(p))
     return p
+
+
+NEOX, INTERLEAVED = 0, 1
+
+
+def rmsnorm(x, gamma=None, eps: float = 0.0) -> np.ndarray:
+    """RmsNorm of every row of x [..., width] (CANN aclnnMlaProlog, RmsNorm
+    formula): gamma * x / sqrt(mean(x^2) + eps).  float64 result."""
+    x = _c(x)
+    width = x.shape[-1]
+    n_rows = x.size // width if width else 0
+    y = np.empty(x.shape, np.float64)
+    g = None if gamma is None else _c(gamma)
+    _load().mla_oracle_rmsnorm(_p(x), _code(x), n_rows, width, _p(g), 0 if g is None else _code(g),
+                               float(eps), _p(y))
+    return y
+
+
+def rope_rows(x, positions, base: float, style: int = NEOX) -> np.ndarray:
+    """RoPE of x [n_rows][n_heads][n_dims], every head of row r at position
+    positions[r] (mla.rs rope_neox / rope_interleaved).  float64 result."""
+    x = _c(x)
+    n_rows, n_heads, n_dims = x.shape
+    pos = _c(np.asarray(positions, dtype=np.int32))
+    assert pos.shape == (n_rows,)
+    y = np.empty(x.shape, np.float64)
+    _load().mla_oracle_rope_rows(_p(x), _code(x), n_rows, n_heads, n_dims, _p(pos), float(base),
+                                 int(style), _p(y))
+    return y
+
+
+def cache_append(cache_rows, kv_rank: int, c_kv, k_pe, gamma, eps: float, positions,
+                 base: float, style: int, slots):
+    """Cache-append prolog (vLLM cpu_mla do_kv_cache_update, fed by the
+    aclnnMlaProlog c^KV = RmsNorm(.) and k^R = ROPE(.) formulas).
+
+    cache_rows: float64 [num_slots][kv_rank + d_rope], updated in place.  Row
+    slots[n] becomes [RmsNorm(c_kv[n]) | rope(k_pe[n], positions[n])];
+    negative slots are skipped, slots >= num_slots are skipped and counted.
+    Returns the count of out-of-range slots.
+    """
+    assert cache_rows.dtype == np.float64 and cache_rows.flags.c_contiguous
+    num_slots, width = cache_rows.shape
+    d_rope = width - kv_rank
+    c_kv = _c(c_kv)
+    n_tok = c_kv.size // kv_rank
+    k_pe = _c(k_pe) if d_rope else np.zeros(1, c_kv.dtype)
+    pos = _c(np.asarray(positions, dtype=np.int32)) if d_rope else np.zeros(max(n_tok, 1), np.int32)
+    sl = _c(np.asarray(slots, dtype=np.int64))
+    assert sl.shape == (n_tok,)
+    g = None if gamma is None else _c(gamma)
+    bad = _load().mla_oracle_cache_append(
+        kv_rank, d_rope, n_tok, _p(c_kv), _p(k_pe), _code(c_kv), _p(g),
+        0 if g is None else _code(g), float(eps), _p(pos), float(base), int(style), _p(sl),
+        _p(cache_rows), num_slots)
+    return int(bad)

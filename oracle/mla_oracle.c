@@ -24,6 +24,8 @@
  *              MlaDecodeAttentionKernel.
  *   [vllm cpu] vLLM API page "vllm.v1.attention.backends.mla.cpu_mla":
  *              CPUMLABackend, CPUMLAImpl.forward_mqa, do_kv_cache_update.
+ *   [prolog]   Huawei CANN operator page "aclnnMlaProlog": the RmsNorm formula
+ *              and the c^KV / k^R cache formulas.
  *
  * Pins (what each function is checked against, outside itself) are listed in
  * the test file that exercises it; every function below is pinned.
@@ -509,4 +511,88 @@ void mla_oracle_norm_to_neox_perm(int n_dims, int32_t* perm) {
     perm[2 * j] = j;
     perm[2 * j + 1] = j + half;
   }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cache-append prolog: RmsNorm of the latent rows, rope of the rope rows,   */
+/* slot-mapped write into the paged cache.                                   */
+/* ------------------------------------------------------------------------ */
+
+/* [prolog] RmsNorm formula: y_i = gamma_i * x_i / RMS(x), with
+ * RMS(x) = sqrt(mean_i x_i^2 + eps) (eps inside the root).  x [n_rows][width];
+ * gamma [width] or NULL for all ones; y [n_rows][width] (double). */
+void mla_oracle_rmsnorm(const void* x, int x_dt, int64_t n_rows, int width, const void* gamma, int g_dt,
+                        double eps, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double ss = 0.0;
+    for (int i = 0; i < width; ++i) {
+      const double v = ld(x, x_dt, r * width + i);
+      ss += v * v;
+    }
+    const double rms = sqrt(ss / width + eps);
+    for (int i = 0; i < width; ++i) {
+      const double gi = gamma ? ld(gamma, g_dt, i) : 1.0;
+      y[r * width + i] = gi * ld(x, x_dt, r * width + i) / rms;
+    }
+  }
+}
+
+/* Rope of rows x [n_rows][n_heads][n_dims], every head of row r at position
+ * pos[r] ([mla.rs] rope_neox for style 0, rope_interleaved for style 1), into
+ * y (double, same layout). */
+void mla_oracle_rope_rows(const void* x, int x_dt, int64_t n_rows, int n_heads, int n_dims, const int32_t* pos,
+                          double base, int style, double* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    for (int h = 0; h < n_heads; ++h) {
+      double* row = y + (r * n_heads + h) * n_dims;
+      for (int i = 0; i < n_dims; ++i) row[i] = ld(x, x_dt, (r * n_heads + h) * n_dims + i);
+      if (style == 0) mla_oracle_rope_neox(row, n_dims, (double)pos[r], base);
+      else mla_oracle_rope_interleaved(row, n_dims, (double)pos[r], base);
+    }
+  }
+}
+
+/* [vllm cpu] do_kv_cache_update, fed by the prolog's RmsNorm and rope
+ * ([prolog] c^KV and k^R formulas): for each new token n with
+ * slots[n] >= 0, cache row slots[n] (a flat row index block * block_size +
+ * offset) becomes [RmsNorm(c_kv[n]) | rope(k_pe[n], pos[n])].  Tokens with a
+ * negative slot are skipped; slots at or past num_slots are skipped and
+ * counted (the return value).  cache is [num_slots][kv_rank + d_rope] double,
+ * updated in place. */
+int64_t mla_oracle_cache_append(int kv_rank, int d_rope, int64_t n_tok, const void* c_kv, const void* k_pe,
+                                int in_dt, const void* gamma, int g_dt, double eps, const int32_t* pos,
+                                double base, int style, const int64_t* slots, double* cache, int64_t num_slots) {
+  const int D = kv_rank + d_rope;
+  int64_t bad = 0;
+  double* c = (double*)malloc(sizeof(double) * (size_t)(kv_rank > 0 ? kv_rank : 1));
+  double* k = (double*)malloc(sizeof(double) * (size_t)(d_rope > 0 ? d_rope : 1));
+  for (int64_t n = 0; n < n_tok; ++n) {
+    const int64_t slot = slots[n];
+    if (slot < 0) continue;
+    if (slot >= num_slots) {
+      ++bad;
+      continue;
+    }
+    double ss = 0.0;
+    for (int i = 0; i < kv_rank; ++i) {
+      const double v = ld(c_kv, in_dt, n * kv_rank + i);
+      ss += v * v;
+    }
+    const double rms = sqrt(ss / kv_rank + eps);
+    for (int i = 0; i < kv_rank; ++i)
+      c[i] = (gamma ? ld(gamma, g_dt, i) : 1.0) * ld(c_kv, in_dt, n * kv_rank + i) / rms;
+    for (int i = 0; i < d_rope; ++i) k[i] = ld(k_pe, in_dt, n * d_rope + i);
+    if (d_rope > 0) {
+      if (style == 0) mla_oracle_rope_neox(k, d_rope, (double)pos[n], base);
+      else mla_oracle_rope_interleaved(k, d_rope, (double)pos[n], base);
+    }
+    double* dst = cache + slot * D;
+    for (int i = 0; i < kv_rank; ++i) dst[i] = c[i];
+    for (int i = 0; i < d_rope; ++i) dst[kv_rank + i] = k[i];
+  }
+  free(c);
+  free(k);
+  return bad;
 }
