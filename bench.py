@@ -139,6 +139,73 @@ def cpu_baseline(spec, case, figs, max_items: int):
     }
 
 
+def append_bytes(spec, n_tok: int, with_q: bool) -> int:
+    """Algorithmic bytes of one cache append of n_tok tokens (all written):
+    c_kv and k_pe read, the cache row written, q_pe read and written,
+    position and slot read, gamma read once."""
+    e = 2 if spec.dtype == "bf16" else 4
+    per_tok = (spec.kv_rank + spec.d_rope) * e * 2 + 4 + 8
+    if with_q and spec.d_rope:
+        per_tok += 2 * spec.n_head * spec.d_rope * e
+    return n_tok * per_tok + spec.kv_rank * e
+
+
+def time_prolog(spec, case, dims, kv, stream, reps: int = 20, chunk: int = 4096):
+    """The cache-append prolog timed on its own (HIP events on its stream):
+    the decode step's new tokens written into the step's cache, and a
+    prefill-sized chunk of `chunk` tokens written into a cache of its own."""
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_latent_cache_amd as mla
+
+    def dev(a):
+        if a is None or a.size == 0:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def timed(args_):
+        c, k, q, g, pos, slots, cache = args_
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for _ in range(3):
+            mla.mla_cache_append(dims, c, k, g, mi.RMS_EPS, pos, mi.ROPE_BASE, mla.MLA_ROPE_NEOX, q, slots, cache,
+                                 None, stream)
+        for a, b in es:
+            a.record(stream)
+            mla.mla_cache_append(dims, c, k, g, mi.RMS_EPS, pos, mi.ROPE_BASE, mla.MLA_ROPE_NEOX, q, slots, cache,
+                                 None, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in es) / reps * 1e-3  # seconds
+
+    ap = mi.step_append(spec, case.seq_lens, case.block_table)
+    n_step = ap.slots.shape[0]
+    step_args = (dev(ap.c_kv), dev(ap.k_pe), dev(ap.q_pe), dev(ap.gamma),
+                 torch.from_numpy(ap.positions).cuda(), torch.from_numpy(ap.slots).cuda(), kv)
+    t_step = timed(step_args)
+    c, k, q, g = mi.append_values(spec, chunk, tag="bench_chunk")
+    cache = torch.empty(chunk // 16, 16, spec.D, dtype=kv.dtype, device="cuda")
+    chunk_args = (dev(c), dev(k), dev(q), dev(g), torch.arange(chunk, dtype=torch.int32, device="cuda"),
+                  torch.arange(chunk, dtype=torch.int64, device="cuda"), cache)
+    t_chunk = timed(chunk_args)
+    b_step = append_bytes(spec, n_step, True)
+    b_chunk = append_bytes(spec, chunk, True)
+    return {
+        "kernel": "cache_append_kernel (RmsNorm + rope + slot-mapped write, q_pe rope in place)",
+        "decode_step_tokens": n_step,
+        "decode_step_us": round(t_step * 1e6, 2),
+        "decode_step_bytes": b_step,
+        "chunk_tokens": chunk,
+        "chunk_us": round(t_chunk * 1e6, 2),
+        "chunk_bytes": b_chunk,
+        "chunk_gbs": round(b_chunk / t_chunk / 1e9, 1),
+        "chunk_frac": round(b_chunk / t_chunk / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +350,9 @@ def main() -> int:
             stage[name] = sum(a.elapsed_time(b) for a, b in es) / len(es)
     stage["decode"] = dec_avg
 
+    prolog = time_prolog(spec, case, dims, copies[0]["kv"], stream)
+    stage["cache_append"] = prolog["decode_step_us"] * 1e-3
+
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -319,6 +389,7 @@ def main() -> int:
         "tokens_heads_per_s": round(figs["tokens_heads"] / (ms_step * 1e-3), 1),
         "step_launch": "host launches" if args.eager else "HIP graph replay (absorb, split, merge, decompress)",
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "prolog": prolog,
         "roofline": {
             "kernel": "decode call: decode_split_mfma + decode_merge",
             "bound": "hbm",

@@ -10,14 +10,20 @@
  *                            an LSE-weighted merge of the splits
  *   3. mla_decompress_v      out[n][h] = W_UV[h] o_lat[n][h]
  *
+ * and, upstream of step 2, the cache-append prolog mla_cache_append (RmsNorm
+ * of the new latent rows, rope of their k_pe and of the query rope part, and
+ * the slot-mapped write into the paged cache).
+ *
  * Pages this interface follows (cited by title and section):
  *   memra-engine 0.124.0 source page "mla.rs": MlaDims (geometry), MlaDims::scale,
  *     MlaInputs (layouts and the causal suffix rule), mla_attend_absorbed.
  *   vllm.cpp source page "cpu_mla_attn.cpp": MlaDecodeAttentionKernel (argument
  *     list, paged addressing, LSE definition, zeros for an empty request).
  *   vLLM API page "vllm.v1.attention.backends.mla.cpu_mla": CPUMLABackend (head
- *     size 576 = 512 + 64, block size 16), CPUMLAImpl.forward_mqa (decode call).
- *   CANN page "aclnnMlaProlog": two-phase call (workspace size, then execute).
+ *     size 576 = 512 + 64, block size 16), CPUMLAImpl.forward_mqa (decode call),
+ *     do_kv_cache_update (slot-mapped cache write, padding slots skipped).
+ *   CANN page "aclnnMlaProlog": two-phase call (workspace size, then execute);
+ *     the RmsNorm formula and the c^KV / k^R / q^R formulas.
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is DEVICE memory owned by the caller; the library
@@ -159,6 +165,55 @@ mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch
 mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_lat,
                             mla_dtype o_dt, const void* w_uv, mla_dtype w_dt, void* out,
                             mla_dtype out_dt, void* stream);
+
+/* Rope pairing (memra mla.rs, rope_neox and rope_interleaved): NEOX rotates
+ * the pair (x[j], x[j + d/2]), interleaved ("NORM") the pair (x[2j], x[2j+1]),
+ * both by the angle pos * base^(-2j/d), d = d_rope, j < d/2.  A model whose
+ * weights expect interleaved rope can run NEOX after permuting the rope rows
+ * of its projection weights once at load time (mla.rs, norm_to_neox_perm):
+ * query-key dot products are unchanged. */
+typedef enum mla_rope_style { MLA_ROPE_NEOX = 0, MLA_ROPE_INTERLEAVED = 1 } mla_rope_style;
+
+/* Data-error bit of mla_cache_append. */
+#define MLA_DATA_BAD_SLOT 0x10u /* a slot_mapping entry >= num_blocks * block_size */
+
+/* Cache-append prolog: write the new tokens' latent rows into the paged cache
+ * and rotate their query rope part (vLLM cpu_mla, do_kv_cache_update; CANN
+ * aclnnMlaProlog, the formulas c^KV = RmsNorm(x W^DKV), k^C = Cache(c^KV),
+ * k^R = Cache(ROPE(x W^KR)) and q^R = ROPE(.), applied to the projections the
+ * caller passes in).  For each token n < n_tok with s = slot_mapping[n]:
+ *   s >= 0:  cache row s (= kv_cache[s / 16][s % 16], all D = kv_rank + d_rope
+ *            columns) becomes
+ *              [ gamma * c_kv[n] / sqrt(mean(c_kv[n]^2) + eps) | rope(k_pe[n], p) ]
+ *            with p = positions[n] and the pairing rope_style;
+ *   s < 0:   padding token, no cache write;
+ *   s >= num_blocks * 16: no cache write, MLA_DATA_BAD_SLOT is ORed into
+ *            *data_err (when data_err is not NULL).
+ *   q_pe[n][h] = rope(q_pe[n][h], p) for every head h, whatever s is.
+ * c_kv   [n_tok][kv_rank], before RmsNorm, type in_dt
+ * k_pe   [n_tok][d_rope], before rope, type in_dt (NULL allowed when d_rope == 0)
+ * gamma  [kv_rank] type in_dt, or NULL for all ones
+ * positions int32 [n_tok] (NULL allowed when d_rope == 0)
+ * q_pe   [n_tok][n_head][d_rope] type in_dt, rotated in place, or NULL to
+ *        leave the queries alone
+ * slot_mapping int64 [n_tok]: flat cache row block * 16 + offset, or -1
+ * kv_cache [num_blocks][block_size][D] type kv_dt; rows not named by a
+ *        valid slot are not touched
+ * data_err device uint32, or NULL; never cleared by the library
+ * Arithmetic: float32 for the norm and the rotation; each angle is formed in
+ * double and reduced to [-pi, pi] before the float sine and cosine.  Two
+ * tokens naming the same slot leave that row in an unspecified mix of both.
+ * Errors: MLA_ERR_NULL, MLA_ERR_DIMS (kv_rank < 1, d_rope < 0 or odd, n_head
+ * < 1 with q_pe), MLA_ERR_SHAPE (n_tok < 0, num_blocks < 1), MLA_ERR_UNSUPPORTED
+ * (block_size != 16, d_rope > 256), MLA_ERR_ARG (eps negative or not finite,
+ * rope_base not finite or <= 0 when d_rope > 0, bad rope_style or dtype
+ * code), MLA_ERR_HIP. */
+mla_status mla_cache_append(const mla_dims* dims, int64_t n_tok, const void* c_kv, const void* k_pe,
+                            const void* gamma, mla_dtype in_dt, float eps, const int32_t* positions,
+                            double rope_base, int32_t rope_style, void* q_pe,
+                            const int64_t* slot_mapping, void* kv_cache, mla_dtype kv_dt,
+                            int64_t num_blocks, int32_t block_size, uint32_t* data_err,
+                            void* stream);
 
 /* Waits for `stream`, then ORs the MLA_DATA_* bits that the most recent
  * mla_decode_attention call on this workspace recorded into *flags (0 = no

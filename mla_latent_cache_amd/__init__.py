@@ -3,22 +3,28 @@
 The hot path is three library calls, each a hand-written HIP kernel set:
 ``mla_absorb_q`` (fold W_UK into the query), ``mla_decode_attention`` (split-KV
 attention over the paged latent cache plus the LSE-weighted merge) and
-``mla_decompress_v`` (one W_UV decompression).  See include/mla.h for the
-contract of every entry point.
+``mla_decompress_v`` (one W_UV decompression).  Upstream of attention,
+``mla_cache_append`` writes the new tokens' RmsNorm'd and rope'd latent rows
+into the paged cache and rotates the query rope part.  See include/mla.h for
+the contract of every entry point.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     MLA_BF16,
     MLA_DATA_BAD_BLOCK,
+    MLA_DATA_BAD_SLOT,
     MLA_DATA_LEN_BELOW_TQ,
     MLA_DATA_LEN_OVER_TABLE,
     MLA_DATA_NEG_LEN,
     MLA_F32,
+    MLA_ROPE_INTERLEAVED,
+    MLA_ROPE_NEOX,
     MlaError,
     as_dims,
     lib,
     mla_absorb_q,
+    mla_cache_append,
     mla_decode_attention,
     mla_decode_resolve_splits,
     mla_decode_status,

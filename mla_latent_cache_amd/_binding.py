@@ -19,10 +19,12 @@ MLA_F32, MLA_BF16 = 0, 1
 MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE = 0, 1, 2, 3
 MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP, MLA_ERR_ARG = 4, 5, 6, 7
 MLA_DATA_NEG_LEN, MLA_DATA_LEN_OVER_TABLE, MLA_DATA_LEN_BELOW_TQ, MLA_DATA_BAD_BLOCK = 1, 2, 4, 8
+MLA_DATA_BAD_SLOT = 0x10
+MLA_ROPE_NEOX, MLA_ROPE_INTERLEAVED = 0, 1
 
 EXPORTS = ("mla_default_scale", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode_resolve_splits", "mla_decode_attention", "mla_decompress_v",
-           "mla_decode_status", "mla_status_string")
+           "mla_decode_status", "mla_status_string", "mla_cache_append")
 
 
 class MlaError(RuntimeError):
@@ -67,6 +69,9 @@ def lib():
     L.mla_decompress_v.argtypes = [P, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp]
     L.mla_decode_status.restype = ctypes.c_int
     L.mla_decode_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    L.mla_cache_append.restype = ctypes.c_int
+    L.mla_cache_append.argtypes = [P, i64, vp, vp, vp, ctypes.c_int, f32, vp, ctypes.c_double, i32, vp, vp,
+                                   vp, ctypes.c_int, i64, i32, vp, vp]
     L.mla_status_string.restype = ctypes.c_char_p
     L.mla_status_string.argtypes = [ctypes.c_int]
     _LIB = L
@@ -182,6 +187,23 @@ def mla_decode_status(workspace, stream=None) -> int:
     flags = ctypes.c_uint32(0)
     _check("mla_decode_status", lib().mla_decode_status(_ptr(workspace), ctypes.byref(flags), _stream(stream)))
     return int(flags.value)
+
+
+def mla_cache_append(dims: DimsLike, c_kv, k_pe, gamma, eps: float, positions, rope_base: float,
+                     rope_style: int, q_pe, slot_mapping, kv_cache, data_err=None, stream=None) -> None:
+    """Cache-append prolog: kv_cache row slot_mapping[n] <- [RmsNorm(c_kv[n]) |
+    rope(k_pe[n], positions[n])], q_pe rotated in place.  c_kv [n_tok][kv_rank],
+    k_pe [n_tok][d_rope], gamma [kv_rank] or None, positions int32 [n_tok],
+    q_pe [n_tok][H][d_rope] or None, slot_mapping int64 [n_tok], kv_cache
+    [num_blocks][16][D], data_err int32 [1] device tensor or None."""
+    d = as_dims(dims)
+    n_tok = c_kv.numel() // max(1, d.kv_rank)
+    pe = k_pe if (k_pe is not None and k_pe.numel() > 0) else None
+    qpe = q_pe if (q_pe is not None and q_pe.numel() > 0) else None
+    _check("mla_cache_append", lib().mla_cache_append(
+        ctypes.byref(d), n_tok, _ptr(c_kv), _ptr(pe), _ptr(gamma), _dt(c_kv), float(eps), _ptr(positions),
+        float(rope_base), int(rope_style), _ptr(qpe), _ptr(slot_mapping), _ptr(kv_cache), _dt(kv_cache),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(data_err), _stream(stream)))
 
 
 def mla_status_string(code: int) -> str:

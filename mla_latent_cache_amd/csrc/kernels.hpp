@@ -62,4 +62,27 @@ hipError_t launch_decompress(int n_head, int d_v, int kv_rank, int64_t n_tok, co
                              bool o_bf16, const void* w_uv, bool w_bf16, void* out, bool out_bf16,
                              hipStream_t stream);
 
+// One cache-append prolog call (RmsNorm of c_kv, rope of k_pe and q_pe,
+// slot-mapped cache write).  Rope bases are tabulated per launch, so d_rope is
+// at most 2 * kRopeTableMax.
+constexpr int kRopeTableMax = 128;
+
+struct CacheAppend {
+  const void* c_kv;          // [n_tok][kv_rank]
+  const void* k_pe;          // [n_tok][d_rope]
+  const void* gamma;         // [kv_rank] or null
+  void* q_pe;                // [n_tok][n_head][d_rope] or null
+  const int32_t* positions;  // [n_tok]
+  const int64_t* slots;      // [n_tok]
+  void* cache;               // [num_slots][kv_rank + d_rope]
+  uint32_t* err;             // data-error word or null
+  int64_t n_tok, num_slots;
+  int kv_rank, d_rope, n_head;
+  float eps;
+  double rope_base;
+  bool in_bf16, cache_bf16, interleaved;
+};
+
+hipError_t launch_cache_append(const CacheAppend& c, hipStream_t stream);
+
 }  // namespace mla

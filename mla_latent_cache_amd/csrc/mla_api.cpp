@@ -214,6 +214,49 @@ mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_l
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status mla_cache_append(const mla_dims* dims, int64_t n_tok, const void* c_kv, const void* k_pe,
+                            const void* gamma, mla_dtype in_dt, float eps, const int32_t* positions,
+                            double rope_base, int32_t rope_style, void* q_pe, const int64_t* slot_mapping,
+                            void* kv_cache, mla_dtype kv_dt, int64_t num_blocks, int32_t block_size,
+                            uint32_t* data_err, void* stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (dims->kv_rank < 1 || dims->d_rope < 0 || dims->d_rope % 2 != 0 || (q_pe && dims->n_head < 1))
+    return MLA_ERR_DIMS;
+  if (n_tok < 0 || num_blocks < 1) return MLA_ERR_SHAPE;
+  if (block_size != 16) return MLA_ERR_UNSUPPORTED;
+  if (dims->d_rope > 2 * mla::kRopeTableMax) return MLA_ERR_UNSUPPORTED;
+  if (!dt_ok(in_dt) || !dt_ok(kv_dt)) return MLA_ERR_ARG;
+  if (!(eps >= 0.f) || !isfinite(eps)) return MLA_ERR_ARG;
+  if (rope_style != MLA_ROPE_NEOX && rope_style != MLA_ROPE_INTERLEAVED) return MLA_ERR_ARG;
+  if (dims->d_rope > 0 && (!(rope_base > 0.0) || !isfinite(rope_base))) return MLA_ERR_ARG;
+  if (num_blocks > INT64_MAX / block_size) return MLA_ERR_SHAPE;
+  if (n_tok == 0) return MLA_OK;
+  if (!c_kv || !slot_mapping || !kv_cache) return MLA_ERR_NULL;
+  if (dims->d_rope > 0 && (!k_pe || !positions)) return MLA_ERR_NULL;
+  mla::CacheAppend c = {};
+  c.c_kv = c_kv;
+  c.k_pe = k_pe;
+  c.gamma = gamma;
+  c.q_pe = dims->d_rope > 0 ? q_pe : nullptr;
+  c.positions = positions;
+  c.slots = slot_mapping;
+  c.cache = kv_cache;
+  c.err = data_err;
+  c.n_tok = n_tok;
+  c.num_slots = num_blocks * block_size;
+  c.kv_rank = dims->kv_rank;
+  c.d_rope = dims->d_rope;
+  c.n_head = dims->n_head;
+  c.eps = eps;
+  c.rope_base = rope_base;
+  c.in_bf16 = in_dt == MLA_BF16;
+  c.cache_bf16 = kv_dt == MLA_BF16;
+  c.interleaved = rope_style == MLA_ROPE_INTERLEAVED;
+  const hipError_t e = mla::launch_cache_append(c, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return MLA_ERR_SHAPE;
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status mla_decode_status(const void* workspace, uint32_t* flags, void* stream) {
   if (!workspace || !flags) return MLA_ERR_NULL;
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return MLA_ERR_HIP;

@@ -109,6 +109,46 @@ def test_absorb_and_decompress_host_validation():
     assert L.mla_decode_status(None, None, None) == B.MLA_ERR_NULL
 
 
+def append(**kw):
+    a = dict(dims=dims(), n_tok=4, c_kv=FAKE, k_pe=FAKE, gamma=None, in_dt=B.MLA_BF16, eps=1e-6, pos=FAKE,
+             base=8e6, style=B.MLA_ROPE_NEOX, q_pe=FAKE, slots=FAKE, cache=FAKE, kv_dt=B.MLA_BF16,
+             num_blocks=10, block_size=16, err=None, stream=None)
+    a.update(kw)
+    return mla.lib().mla_cache_append(a["dims"], a["n_tok"], a["c_kv"], a["k_pe"], a["gamma"], a["in_dt"],
+                                      a["eps"], a["pos"], a["base"], a["style"], a["q_pe"], a["slots"],
+                                      a["cache"], a["kv_dt"], a["num_blocks"], a["block_size"], a["err"],
+                                      a["stream"])
+
+
+def test_cache_append_host_validation():
+    assert append(dims=None) == B.MLA_ERR_NULL
+    assert append(dims=dims((64, 192, 64, 256, 0))) == B.MLA_ERR_DIMS
+    assert append(dims=dims((64, 192, -2, 256, 512))) == B.MLA_ERR_DIMS
+    assert append(dims=dims((64, 192, 63, 256, 512))) == B.MLA_ERR_DIMS   # odd rope width
+    assert append(dims=dims((0, 192, 64, 256, 512))) == B.MLA_ERR_DIMS    # heads needed for q_pe
+    assert append(n_tok=-1) == B.MLA_ERR_SHAPE
+    assert append(num_blocks=0) == B.MLA_ERR_SHAPE
+    assert append(block_size=32) == B.MLA_ERR_UNSUPPORTED
+    assert append(dims=dims((64, 192, 258, 256, 512))) == B.MLA_ERR_UNSUPPORTED
+    assert append(in_dt=5) == B.MLA_ERR_ARG
+    assert append(kv_dt=-1) == B.MLA_ERR_ARG
+    assert append(eps=-1e-6) == B.MLA_ERR_ARG
+    assert append(eps=math.nan) == B.MLA_ERR_ARG
+    assert append(eps=math.inf) == B.MLA_ERR_ARG
+    assert append(base=0.0) == B.MLA_ERR_ARG
+    assert append(base=math.inf) == B.MLA_ERR_ARG
+    assert append(style=2) == B.MLA_ERR_ARG
+    assert append(c_kv=None) == B.MLA_ERR_NULL
+    assert append(slots=None) == B.MLA_ERR_NULL
+    assert append(cache=None) == B.MLA_ERR_NULL
+    assert append(k_pe=None) == B.MLA_ERR_NULL
+    assert append(pos=None) == B.MLA_ERR_NULL
+    assert append(n_tok=0, c_kv=None, k_pe=None, pos=None, q_pe=None, slots=None, cache=None) == B.MLA_OK
+    # No rope part: k_pe, positions and rope base are not needed.
+    nope = (64, 256, 0, 256, 512)
+    assert append(dims=dims(nope), n_tok=0, k_pe=None, pos=None, base=0.0) == B.MLA_OK
+
+
 def test_default_scale_and_strings():
     assert mla.mla_default_scale(GLM52) == pytest.approx(1 / 16, abs=1e-9)
     assert mla.mla_default_scale((64, 256, 0, 256, 512)) == pytest.approx(1 / 16, abs=1e-9)
