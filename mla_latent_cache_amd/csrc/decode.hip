@@ -23,7 +23,8 @@
 //   * wave (qh, dq) then accumulates output columns [128 dq, 128 dq + 128) of
 //     its 32 query rows, reading V^T from the same LDS tile with the
 //     transposing ds_read_b64_tr_b16; this PV step of tile t runs in the same
-//     phase as the S step of tile t + 1.
+//     phase as the softmax of tile t + 1 (P^T and the rescale factors are
+//     double-buffered by tile parity).
 // Two waves share each SIMD, so one wave's LDS reads overlap the other's MFMAs.
 // With one range per request the workgroup writes the final output and LSE;
 // otherwise it writes (o, lse) partials and decode_merge combines them:
@@ -105,6 +106,7 @@ __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("" ::: "memory");
 }
 
+
 constexpr float kSlack = 8.f;   // log2 headroom before the softmax reference moves
 
 // Two 8-byte LDS reads at lds_addr + OFF and + OFF + 32, as separate
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   constexpr int PLANE = 72;  // plane pitch in 8-byte units
   __shared__ __attribute__((aligned(16))) u32x4 ring[3 * T::IMG];  // three tile buffers
   __shared__ __attribute__((aligned(16))) uint2 xs[8][2][4][PLANE];  // S partials [wave][half][n * 2 + rt][lane]
-  __shared__ __attribute__((aligned(16))) uint2 pb[2][2][2][PLANE];  // bf16 P^T [qh][n][rt][lane]
-  __shared__ float al[64];                                           // per-query rescale of the output
+  __shared__ __attribute__((aligned(16))) uint2 pb[2][2][2][2][PLANE];  // bf16 P^T [parity][qh][n][rt][lane]
+  __shared__ float al[2][64];                                          // per-query rescale [parity][query]
   __shared__ float fin[64];                                          // per-query 1 / l at the end
 
   write_header(a);
@@ -285,12 +287,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
 
   // O^T += V^T P^T for tile image `img`, after rescaling by the factors the
   // softmax step published with P.
-  auto pv = [&](const u32x4* img) {
-    const uint2 p00 = pb[qh][0][0][lane], p01 = pb[qh][0][1][lane];
-    const uint2 p10 = pb[qh][1][0][lane], p11 = pb[qh][1][1][lane];
+  auto pv = [&](const u32x4* img, int par) {
+    const uint2 p00 = pb[par][qh][0][0][lane], p01 = pb[par][qh][0][1][lane];
+    const uint2 p10 = pb[par][qh][1][0][lane], p11 = pb[par][qh][1][1][lane];
     const bf16x8 pB0 = as_bf16x8(u32x4{p00.x, p00.y, p01.x, p01.y});
     const bf16x8 pB1 = as_bf16x8(u32x4{p10.x, p10.y, p11.x, p11.y});
-    const float al0 = al[32 * qh + l16], al1 = al[32 * qh + 16 + l16];
+    const float al0 = al[par][32 * qh + l16], al1 = al[par][32 * qh + 16 + l16];
     if (__ballot(al0 != 1.f || al1 != 1.f)) {
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
@@ -386,8 +388,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
     lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     const uint2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    pb[qh][nf][rt_f][src_lane] = pk;
-    if (lane < 8) al[fq] = alpha;
+    pb[t & 1][qh][nf][rt_f][src_lane] = pk;
+    if (lane < 8) al[t & 1][fq] = alpha;
   };
 
   // Prologue: tile 0's loads go out first, then the queries, then tile 1; the
@@ -426,30 +428,24 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   }
   if (n_tiles > 0) barrier_keep_loads();
   int cur = 0;  // ring slot of tile t
+  // Phase 1 of tile t: partial S^T of tile t.  Phase 2: softmax of tile t and
+  // PV of tile t - 1 (its P^T was published one phase earlier), so the matrix
+  // cores have work while the softmax waits on LDS.  Tile t + 2 is issued once
+  // tile t - 1 is no longer read, after the second barrier.
   for (int t = 0; t < n_tiles; ++t) {
-    const int prev = cur == 0 ? 2 : cur - 1, nxt2 = prev;  // tile t + 2 reuses tile t - 1's slot
+    const int prev = cur == 0 ? 2 : cur - 1;  // tile t - 1's slot, reused by tile t + 2
     const bool more = t + 2 < n_tiles;
-    if (more) tile_ids(t + 2, ids);  // scalar loads, complete by the barrier below
-    if (t > 0) pv(ring + prev * T::IMG);
+    if (more) tile_ids(t + 2, ids);  // scalar loads, complete by the barriers below
     s_part(ring + cur * T::IMG);
-    barrier_keep_loads();  // partials visible; tile t - 1 no longer read
-    if (more) issue_tile(t + 2, ids, ring + nxt2 * T::IMG);
+    barrier_keep_loads();  // partials visible
     softmax(t);
-    if (t + 1 < n_tiles) {  // tile t + 1 resident
-      if (more) {
-        switch (c_w) {
-          case 5: wait_vmcnt<5>(); break;
-          case 4: wait_vmcnt<4>(); break;
-          default: wait_vmcnt<0>(); break;
-        }
-      } else {
-        wait_vmcnt<0>();
-      }
-    }
-    barrier_keep_loads();  // P^T and rescale factors visible
+    if (t > 0) pv(ring + prev * T::IMG, (t - 1) & 1);
+    if (t + 1 < n_tiles) wait_vmcnt<0>();
+    barrier_keep_loads();  // P^T visible; tile t + 1 resident; tile t - 1 no longer read
+    if (more) issue_tile(t + 2, ids, ring + prev * T::IMG);
     cur = cur == 2 ? 0 : cur + 1;
   }
-  if (n_tiles > 0) pv(ring + (cur == 0 ? 2 : cur - 1) * T::IMG);
+  if (n_tiles > 0) pv(ring + (cur == 0 ? 2 : cur - 1) * T::IMG, (n_tiles - 1) & 1);
 
   // Final normalisation: the owner lanes of each query sum their partial l,
   // publish 1 / l, and write the LSE.
