@@ -392,27 +392,41 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     if (lane < 8) al[t & 1][fq] = alpha;
   };
 
-  // Prologue: tile 0's loads go out first, then the queries, then tile 1; the
-  // wait leaves only tile 1 in flight.
+  auto q_swizzle = [](int r) { return CH % 16 == 0 ? (r & 15) : ((r >> 1) & 7); };
+  // Prologue: tile 0's loads go out first, then the workgroup's 64 query rows,
+  // then tile 1; the wait leaves only tile 1 in flight.  The query rows go
+  // HBM -> LDS with the same 1 KB coalesced loads as the tiles -- rows 0..31
+  // into the third ring buffer (first used by tile 2), rows 32..63 into the
+  // partial-exchange planes (first written by the S step of tile 0) -- and each
+  // wave then reads its B operands from there; rows past n_q read as zeros.
+  // (Loading the operands straight from global memory, 8 scattered bytes per
+  // lane, costs several times the address work of a tile.)
   int32_t ids[2];
   if (n_tiles > 0) {
     tile_ids(0, ids);
     issue_tile(0, ids, ring);
-  }
-  // Queries: B operand of S^T for this wave's k-steps (see qf).
+    constexpr int Q_LOADS = 64 * D * 2 / 1024;  // 1 KB wave-loads of 64 query rows
+    constexpr int Q_HALF = Q_LOADS / 2;
+    static_assert(Q_LOADS % 8 == 0 && Q_HALF * 1024 == 32 * D * 2, "query rows split evenly over eight waves and two halves");
+    static_assert(Q_HALF * 1024 <= T::IMG * 16 && Q_HALF * 1024 <= (int)sizeof(xs), "query staging fits");
+    const int q_valid = a.n_q - mt * kQRowsPerWG < kQRowsPerWG ? a.n_q - mt * kQRowsPerWG : kQRowsPerWG;
+    const i32x4 qrs = raw_rsrc(static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + (int64_t)mt * kQRowsPerWG) * D,
+                               (uint32_t)(q_valid * D * 2));
+    const uint32_t q_lds0 = lds_addr(ring + 2 * T::IMG), q_lds1 = lds_addr(xs);
+    static_assert(CH % 16 == 0 || CH % 16 == 8, "staged query rows need a 1024- or 1152-byte-class pitch");
+    // Staged row r (of a half) keeps its 16-byte chunk c at position c ^ sw(r),
+    // so that the 16 rows read at one column fall on different banks: with a
+    // 1152-byte pitch (rope width 64) rows already alternate between two bank
+    // halves and sw(r) = (r >> 1) & 7; with a 1024-byte pitch every row starts
+    // on the same bank and sw(r) = r & 15.
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const uint16_t* qp =
-        static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + q_row[n]) * D + 32 * dq + 4 * g;
-#pragma unroll
-    for (int j = 0; j < KQ; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q_ok[n] && j < nk) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(qp + 128 * j);
-        const uint2 hi = *reinterpret_cast<const uint2*>(qp + 128 * j + 16);
-        v = u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-      qf[n][j] = as_bf16x8(v);
+    for (int i = 0; i < Q_LOADS / 8; ++i) {
+      const int u = w + 8 * i;
+      const int hq = u < Q_HALF ? 0 : 1;
+      const int unit = (u - hq * Q_HALF) * 64 + lane;  // 16-byte position within the half
+      const int r = unit / CH, pc = unit - r * CH;
+      const uint32_t voff = (uint32_t)((32 * hq + r) * D * 2 + (pc ^ q_swizzle(r)) * 16);
+      dma16(qrs, (hq == 0 ? q_lds0 : q_lds1) + (uint32_t)(u - hq * Q_HALF) * 1024u, voff);
     }
   }
   if (n_tiles > 1) {
@@ -426,7 +440,28 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   } else {
     wait_vmcnt<0>();
   }
-  if (n_tiles > 0) barrier_keep_loads();
+  if (n_tiles > 0) {
+    barrier_keep_loads();  // tile 0 and the query rows resident
+    // Queries: B operand of S^T for this wave's k-steps (see qf).
+    const char* qsrc = reinterpret_cast<const char*>(qh == 0 ? (const void*)(ring + 2 * T::IMG) : (const void*)xs);
+    const int qsw = q_swizzle(l16);  // chunk swizzle of rows 16 n + l16 (same for both n)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const char* qp = qsrc + (16 * n + l16) * D * 2 + (g & 1) * 8;
+#pragma unroll
+      for (int j = 0; j < KQ; ++j) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j < nk) {
+          const int c = 4 * (dq + 4 * j) + (g >> 1);  // chunk of columns 32 kk + 4 g
+          const uint2 lo = *reinterpret_cast<const uint2*>(qp + (c ^ qsw) * 16);
+          const uint2 hi = *reinterpret_cast<const uint2*>(qp + ((c + 2) ^ qsw) * 16);
+          v = u32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+        qf[n][j] = as_bf16x8(v);
+      }
+    }
+    barrier_keep_loads();  // staging areas free again
+  }
   int cur = 0;  // ring slot of tile t
   // Phase 1 of tile t: partial S^T of tile t.  Phase 2: softmax of tile t and
   // PV of tile t - 1 (its P^T was published one phase earlier), so the matrix
