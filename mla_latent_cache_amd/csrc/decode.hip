@@ -252,24 +252,30 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     c_w += u < T::TILE_LOADS ? 1 : 0;
   }
 
-  // Issue the loads of tile t (block ids `ids`) into `dst`.
+  // Issue the loads of tile t (block ids `ids`) into `dst`.  All bounds are
+  // 32-bit scalar arithmetic (a range never holds 2^31 rows, a cache never
+  // 2^31 blocks), and which block a load belongs to is known at compile time
+  // except for the one load that straddles the two blocks.
+  const int range_rows = (int)(r_end - r_begin);
+  const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
   auto issue_tile = [&](int t, const int32_t* ids, u32x4* dst) {
     i32x4 rs[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int32_t id = ids[hb];
-      const int64_t left = r_end - (r_begin + (int64_t)t * 32 + hb * 16);
-      const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
-      const bool ok = id >= 0 && (int64_t)id < a.num_blocks;
+      const int left = range_rows - 32 * t - 16 * hb;
+      const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : left);
+      const bool ok = (uint32_t)id < nb32;
       if (nvalid > 0 && !ok) flags |= kBadBlock;
-      const uint16_t* base = ok ? kv + (int64_t)id * 16 * D : kv;
-      rs[hb] = raw_rsrc(base, ok ? (uint32_t)(nvalid * D * 2) : 0u);
+      rs[hb] = raw_rsrc(kv + (int64_t)(ok ? id : 0) * (16 * D), ok ? (uint32_t)(nvalid * D * 2) : 0u);
     }
     const uint32_t lbase = lds_addr(dst);
 #pragma unroll
     for (int j = 0; j < T::WAVE_LOADS; ++j) {
       const int u = w + 8 * j;
-      if (u < T::TILE_LOADS) dma16(u < T::BLK_LOADS ? rs[0] : rs[1], lbase + (uint32_t)u * 1024u, voffs[j]);
+      const bool in_tile = 8 * j + 7 < T::TILE_LOADS || u < T::TILE_LOADS;
+      const bool blk0 = 8 * j + 7 < T::BLK_LOADS || (8 * j < T::BLK_LOADS && u < T::BLK_LOADS);
+      if (in_tile) dma16(blk0 ? rs[0] : rs[1], lbase + (uint32_t)u * 1024u, voffs[j]);
     }
   };
 
@@ -343,6 +349,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
            constexpr int P = I + kAhead;
            lds_read_b64x2<(P % 2) * T::BLK_IMG * 16 + 256 * (P / 2)>(ka, kr[P / 2][P % 2][0], kr[P / 2][P % 2][1]);
          }
+         // Keep this step's MFMAs between its wait and the next step's wait:
+         // the scheduler would otherwise sink them below all the waits and
+         // serialise the reads and the matrix work.
+         __builtin_amdgcn_sched_barrier(0);
        }()),
        ...);
     }(std::make_integer_sequence<int, NP>{});
@@ -641,6 +651,56 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Workgroups per request in the merge (kMergeRows query rows each).
 __device__ __host__ inline int merge_wg_per_request(int n_q) { return (n_q + kMergeRows - 1) / kMergeRows; }
 
+// Register-resident merge of one query row over S <= KR splits: every LSE and
+// partial vector of the row is loaded at once (one memory latency); lane l owns
+// columns 4 l .. + 3 and 256 + 4 l .. + 3 of a 512-wide row.  Loads past the
+// last split repeat it and are masked out.
+template <int KR>
+__device__ __forceinline__ void merge_row_reg(const DecodeArgs& a, int64_t qrow, const float* lp, const float* op,
+                                              int64_t sstride, int S, int R, int lane) {
+  float lk[KR];
+  f32x4 v0[KR], v1[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const int kk = k < S ? k : S - 1;
+    lk[k] = lp[(int64_t)kk * a.n_q];
+    v0[k] = *reinterpret_cast<const f32x4*>(op + kk * sstride + 4 * lane);
+    v1[k] = *reinterpret_cast<const f32x4*>(op + kk * sstride + 256 + 4 * lane);
+  }
+  float M = -INFINITY;
+  bool any_nan = false;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    if (k < S) {
+      any_nan |= isnan(lk[k]);
+      M = fmaxf(M, lk[k]);
+    }
+  }
+  float wsum = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    const bool live = k < S && lk[k] != -INFINITY && M != -INFINITY;  // empty splits may be unwritten
+    const float wk = live ? __expf(lk[k] - M) : 0.f;
+    wsum += wk;
+    o0 += wk * (live ? v0[k] : f32x4{0.f, 0.f, 0.f, 0.f});
+    o1 += wk * (live ? v1[k] : f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+  const f32x4 r0 = any_nan ? nan4 : o0 * inv, r1 = any_nan ? nan4 : o1 * inv;
+  if (a.out_bf16) {
+    uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * R;
+    *reinterpret_cast<uint2*>(o + 4 * lane) = uint2{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3])};
+    *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = uint2{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+  } else {
+    float* o = static_cast<float*>(a.out) + qrow * R;
+    *reinterpret_cast<f32x4*>(o + 4 * lane) = r0;
+    *reinterpret_cast<f32x4*>(o + 256 + 4 * lane) = r1;
+  }
+  if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
+}
+
 __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   int64_t qrow;  // b * n_q + q
@@ -663,51 +723,12 @@ __global__ __launch_bounds__(64 * kMergeRows) void decode_merge(const DecodeArgs
   const float* op = a.o_part + ((int64_t)b * S * a.n_q + q) * R;
   const int64_t sstride = (int64_t)a.n_q * R;
 
+  if (R == 2 * 256 && S <= 8) {
+    merge_row_reg<8>(a, qrow, lp, op, sstride, S, R, lane);
+    return;
+  }
   if (R == 2 * 256 && S <= kMergeRegSplits) {
-    // Every LSE and partial vector of the row is loaded at once (one memory
-    // latency); lane l owns columns 4 l .. + 3 and 256 + 4 l .. + 3.  Loads past
-    // the last split repeat it and are masked out.
-    float lk[kMergeRegSplits];
-    f32x4 v0[kMergeRegSplits], v1[kMergeRegSplits];
-#pragma unroll
-    for (int k = 0; k < kMergeRegSplits; ++k) {
-      const int kk = k < S ? k : S - 1;
-      lk[k] = lp[(int64_t)kk * a.n_q];
-      v0[k] = *reinterpret_cast<const f32x4*>(op + kk * sstride + 4 * lane);
-      v1[k] = *reinterpret_cast<const f32x4*>(op + kk * sstride + 256 + 4 * lane);
-    }
-    float M = -INFINITY;
-    bool any_nan = false;
-#pragma unroll
-    for (int k = 0; k < kMergeRegSplits; ++k) {
-      if (k < S) {
-        any_nan |= isnan(lk[k]);
-        M = fmaxf(M, lk[k]);
-      }
-    }
-    float wsum = 0.f;
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
-#pragma unroll
-    for (int k = 0; k < kMergeRegSplits; ++k) {
-      const bool live = k < S && lk[k] != -INFINITY && M != -INFINITY;  // empty splits may be unwritten
-      const float wk = live ? __expf(lk[k] - M) : 0.f;
-      wsum += wk;
-      o0 += wk * (live ? v0[k] : f32x4{0.f, 0.f, 0.f, 0.f});
-      o1 += wk * (live ? v1[k] : f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    const f32x4 nan4 = {NAN, NAN, NAN, NAN};
-    const f32x4 r0 = any_nan ? nan4 : o0 * inv, r1 = any_nan ? nan4 : o1 * inv;
-    if (a.out_bf16) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * R;
-      *reinterpret_cast<uint2*>(o + 4 * lane) = uint2{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3])};
-      *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = uint2{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
-    } else {
-      float* o = static_cast<float*>(a.out) + qrow * R;
-      *reinterpret_cast<f32x4*>(o + 4 * lane) = r0;
-      *reinterpret_cast<f32x4*>(o + 256 + 4 * lane) = r1;
-    }
-    if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
+    merge_row_reg<kMergeRegSplits>(a, qrow, lp, op, sstride, S, R, lane);
     return;
   }
 

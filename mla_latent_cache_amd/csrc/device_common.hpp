@@ -94,10 +94,15 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Raw buffer resource (base, size in bytes) as four scalar words.
+// Raw buffer resource (base, size in bytes) as four scalar words.  The words
+// are taken from the first lane: a resource is wave-uniform, and the inline
+// assembly that consumes it needs scalar registers even where the compiler has
+// computed a uniform value in vector registers.
 __device__ __forceinline__ i32x4 raw_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r = {(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)bytes, kRsrcWord3};
+  i32x4 r = {__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+             __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xffffu)),
+             __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3};
   return r;
 }
 
