@@ -34,6 +34,7 @@
 #include "kernels.hpp"
 
 #include <math.h>
+#include <type_traits>
 #include <utility>
 
 namespace mla {
@@ -142,7 +143,7 @@ struct Tile {
   static constexpr int BLK_LOADS = BLK_IMG / 64;
   static constexpr int IMG = 2 * BLK_IMG;                  // one 32-row tile
   static constexpr int TILE_LOADS = 2 * BLK_LOADS;         // 1 KB wave-loads per tile
-  static constexpr int WAVE_LOADS = (TILE_LOADS + 7) / 8;  // per wave and tile (at most)
+  static constexpr int LOADER_LOADS = (TILE_LOADS + 3) / 4;  // per loading wave and tile (at most)
   static constexpr int KSTEPS = D / 32;                    // 32-wide k-steps of S
   static constexpr int KQ = (KSTEPS + 3) / 4;              // k-steps of the largest D quarter
   static constexpr int CT = 8;                             // 16-column output tiles per quarter
@@ -163,6 +164,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   __shared__ __attribute__((aligned(16))) uint2 pb[2][2][2][2][PLANE];  // bf16 P^T [parity][qh][n][rt][lane]
   __shared__ float al[2][64];                                          // per-query rescale [parity][query]
   __shared__ float fin[64];                                          // per-query 1 / l at the end
+  __shared__ uint32_t wflags[8];                                     // data-error bits seen by each wave
 
   write_header(a);
   int b, s, mt, item;
@@ -170,7 +172,13 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int qh = w & 1, dq = w >> 1;                       // query half, D / column quarter
+  // Query half and D / column quarter.  Waves 0-3 (one per SIMD) take the two
+  // quarters with one k-step fewer and issue every tile load; their SIMD
+  // partners 4-7 take the longer quarters and start on the matrix work at
+  // once, so one wave's wait on the load address unit overlaps the other's
+  // MFMAs.
+  const int qh = w & 1, dq = ((w >> 1) + 2) & 3;
+  auto wave_of = [](int h, int d) { return h + 2 * ((d + 2) & 3); };  // wave holding (qh, dq)
   const int l16 = lane & 15, g = lane >> 4;
 
   const int64_t L = a.seq_lens[b];
@@ -235,22 +243,24 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     }
   };
 
-  // This wave's share of the 1 KB wave-loads of a tile image: load u = w + 8 j
-  // covers chunk slots [64 u, 64 u + 64) of the image, i.e. block u / BLK_LOADS.
-  // Rows 8..15 of a block swap the two 16-byte chunks of each 32-byte pair
-  // (bank spreading); slots past a row's end are padding.
-  uint32_t voffs[T::WAVE_LOADS];
-  int c_w = 0;  // this wave's loads per tile (for the vmcnt waits)
-#pragma unroll
-  for (int j = 0; j < T::WAVE_LOADS; ++j) {
-    const int u = w + 8 * j;
+  // The 1 KB wave-loads of a tile image are issued by waves 0-3: load
+  // u = w + 4 j covers chunk slots [64 u, 64 u + 64) of the image, i.e. block
+  // u / BLK_LOADS.  Rows 8..15 of a block swap the two 16-byte chunks of each
+  // 32-byte pair (bank spreading); slots past a row's end are padding.
+  const bool loader = w < 4;
+  auto tile_voff = [&](int u) {  // global byte offset (within its block) of this lane's slot of load u
     const int hb = u / T::BLK_LOADS;
     const int pos = (u - hb * T::BLK_LOADS) * 64 + lane;
     const int rl = pos / STRIDE;
     const int cp = pos - rl * STRIDE;
-    voffs[j] = (rl < 16 && cp < CH) ? (uint32_t)(rl * D + ((cp ^ ((rl >> 3) & 1)) * 8)) * 2u : 0x7ffffff0u;
-    c_w += u < T::TILE_LOADS ? 1 : 0;
-  }
+    return (rl < 16 && cp < CH) ? (uint32_t)(rl * D + ((cp ^ ((rl >> 3) & 1)) * 8)) * 2u : 0x7ffffff0u;
+  };
+  uint32_t voffs[T::LOADER_LOADS];
+#pragma unroll
+  for (int j = 0; j < T::LOADER_LOADS; ++j) voffs[j] = tile_voff(w + 4 * j);
+  int c_w = 0;  // this wave's loads of a prologue tile (for the vmcnt waits)
+#pragma unroll
+  for (int j = 0; j < (T::TILE_LOADS + 7) / 8; ++j) c_w += w + 8 * j < T::TILE_LOADS ? 1 : 0;
 
   // Issue the loads of tile t (block ids `ids`) into `dst`.  All bounds are
   // 32-bit scalar arithmetic (a range never holds 2^31 rows, a cache never
@@ -258,7 +268,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   // except for the one load that straddles the two blocks.
   const int range_rows = (int)(r_end - r_begin);
   const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
-  auto issue_tile = [&](int t, const int32_t* ids, u32x4* dst) {
+  // In the loop only waves 0-3 issue tile loads (u = w + 4 j, offsets voffs);
+  // the two tiles of the prologue are split over all eight waves
+  // (u = w + 8 j, offsets computed on the spot), so that they go out at once.
+  auto issue_tile = [&](int t, const int32_t* ids, u32x4* dst, auto all8) {
+    constexpr bool ALL8 = decltype(all8)::value;
+    if (!ALL8 && !loader) return;
     i32x4 rs[2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -270,14 +285,24 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
       rs[hb] = raw_rsrc(kv + (int64_t)(ok ? id : 0) * (16 * D), ok ? (uint32_t)(nvalid * D * 2) : 0u);
     }
     const uint32_t lbase = lds_addr(dst);
+    if constexpr (ALL8) {
 #pragma unroll
-    for (int j = 0; j < T::WAVE_LOADS; ++j) {
-      const int u = w + 8 * j;
-      const bool in_tile = 8 * j + 7 < T::TILE_LOADS || u < T::TILE_LOADS;
-      const bool blk0 = 8 * j + 7 < T::BLK_LOADS || (8 * j < T::BLK_LOADS && u < T::BLK_LOADS);
-      if (in_tile) dma16(blk0 ? rs[0] : rs[1], lbase + (uint32_t)u * 1024u, voffs[j]);
+      for (int j = 0; j < (T::TILE_LOADS + 7) / 8; ++j) {
+        const int u = w + 8 * j;
+        if (u < T::TILE_LOADS) dma16(u < T::BLK_LOADS ? rs[0] : rs[1], lbase + (uint32_t)u * 1024u, tile_voff(u));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < T::LOADER_LOADS; ++j) {
+        const int u = w + 4 * j;
+        const bool in_tile = 4 * j + 3 < T::TILE_LOADS || u < T::TILE_LOADS;
+        const bool blk0 = 4 * j + 3 < T::BLK_LOADS || (4 * j < T::BLK_LOADS && u < T::BLK_LOADS);
+        if (in_tile) dma16(blk0 ? rs[0] : rs[1], lbase + (uint32_t)u * 1024u, voffs[j]);
+      }
     }
   };
+  using all_waves = std::true_type;
+  using loader_waves = std::false_type;
 
   // Per-lane LDS byte offsets within a tile image.  Tile row r, chunk c lives
   // at chunk slot (r / 16) * BLK_IMG + (r % 16) * STRIDE + (c ^ sw) with
@@ -292,12 +317,10 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   const int v_off = (rr * STRIDE + ((16 * dq + ((l16 & 3) >> 1)) ^ sw_v)) * 16 + (l16 & 1) * 8;
 
   // O^T += V^T P^T for tile image `img`, after rescaling by the factors the
-  // softmax step published with P.
-  auto pv = [&](const u32x4* img, int par) {
-    const uint2 p00 = pb[par][qh][0][0][lane], p01 = pb[par][qh][0][1][lane];
-    const uint2 p10 = pb[par][qh][1][0][lane], p11 = pb[par][qh][1][1][lane];
-    const bf16x8 pB0 = as_bf16x8(u32x4{p00.x, p00.y, p01.x, p01.y});
-    const bf16x8 pB1 = as_bf16x8(u32x4{p10.x, p10.y, p11.x, p11.y});
+  // softmax step published with P.  The rescale (a rare, uniform branch) is a
+  // step of its own so that the products can share a basic block with the
+  // next softmax and interleave with it.
+  auto pv_rescale = [&](int par) {
     const float al0 = al[par][32 * qh + l16], al1 = al[par][32 * qh + 16 + l16];
     if (__ballot(al0 != 1.f || al1 != 1.f)) {
 #pragma unroll
@@ -306,6 +329,12 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
         acc[c][1] *= al1;
       }
     }
+  };
+  auto pv_mma = [&](const u32x4* img, int par) {
+    const uint2 p00 = pb[par][qh][0][0][lane], p01 = pb[par][qh][0][1][lane];
+    const uint2 p10 = pb[par][qh][1][0][lane], p11 = pb[par][qh][1][1][lane];
+    const bf16x8 pB0 = as_bf16x8(u32x4{p00.x, p00.y, p01.x, p01.y});
+    const bf16x8 pB1 = as_bf16x8(u32x4{p10.x, p10.y, p11.x, p11.y});
     const char* vb = reinterpret_cast<const char*>(img) + v_off;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -375,8 +404,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint2 lo = xs[qh + 2 * d][0][nf * 2 + rt_f][src_lane];
-      const uint2 hi = xs[qh + 2 * d][1][nf * 2 + rt_f][src_lane];
+      const uint2 lo = xs[wave_of(qh, d)][0][nf * 2 + rt_f][src_lane];
+      const uint2 hi = xs[wave_of(qh, d)][1][nf * 2 + rt_f][src_lane];
       sc += f32x4{__uint_as_float(lo.x), __uint_as_float(lo.y), __uint_as_float(hi.x), __uint_as_float(hi.y)};
     }
     const int j0 = t * 32 + 16 * rt_f + 4 * g_f;
@@ -399,7 +428,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     const uint2 pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     pb[t & 1][qh][nf][rt_f][src_lane] = pk;
-    if (lane < 8) al[t & 1][fq] = alpha;
+    al[t & 1][fq] = alpha;  // every lane of query fq holds the same factor
   };
 
   auto q_swizzle = [](int r) { return CH % 16 == 0 ? (r & 15) : ((r >> 1) & 7); };
@@ -414,7 +443,7 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   int32_t ids[2];
   if (n_tiles > 0) {
     tile_ids(0, ids);
-    issue_tile(0, ids, ring);
+    issue_tile(0, ids, ring, all_waves{});
     constexpr int Q_LOADS = 64 * D * 2 / 1024;  // 1 KB wave-loads of 64 query rows
     constexpr int Q_HALF = Q_LOADS / 2;
     static_assert(Q_LOADS % 8 == 0 && Q_HALF * 1024 == 32 * D * 2, "query rows split evenly over eight waves and two halves");
@@ -441,8 +470,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   }
   if (n_tiles > 1) {
     tile_ids(1, ids);
-    issue_tile(1, ids, ring + T::IMG);
-    switch (c_w) {
+    issue_tile(1, ids, ring + T::IMG, all_waves{});
+    switch (c_w) {  // tile 1 stays in flight
       case 5: wait_vmcnt<5>(); break;
       case 4: wait_vmcnt<4>(); break;
       default: wait_vmcnt<0>(); break;
@@ -483,17 +512,25 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
     if (more) tile_ids(t + 2, ids);  // scalar loads, complete by the barriers below
     s_part(ring + cur * T::IMG);
     barrier_keep_loads();  // partials visible
+    if (t > 0) pv_rescale((t - 1) & 1);
     softmax(t);
-    if (t > 0) pv(ring + prev * T::IMG, (t - 1) & 1);
+    if (t > 0) pv_mma(ring + prev * T::IMG, (t - 1) & 1);
     if (t + 1 < n_tiles) wait_vmcnt<0>();
     barrier_keep_loads();  // P^T visible; tile t + 1 resident; tile t - 1 no longer read
-    if (more) issue_tile(t + 2, ids, ring + prev * T::IMG);
+    if (more) issue_tile(t + 2, ids, ring + prev * T::IMG, loader_waves{});
     cur = cur == 2 ? 0 : cur + 1;
   }
-  if (n_tiles > 0) pv(ring + (cur == 0 ? 2 : cur - 1) * T::IMG, (n_tiles - 1) & 1);
+  if (n_tiles > 0) {
+    pv_rescale((n_tiles - 1) & 1);
+    pv_mma(ring + (cur == 0 ? 2 : cur - 1) * T::IMG, (n_tiles - 1) & 1);
+  }
 
   // Final normalisation: the owner lanes of each query sum their partial l,
-  // publish 1 / l, and write the LSE.
+  // publish 1 / l, and write the LSE.  Block-id errors are seen only by the
+  // loading waves: every wave takes the union.
+  if (lane == 0) wflags[w] = flags;
+  __syncthreads();
+  flags = wflags[0] | wflags[1] | wflags[2] | wflags[3] | wflags[4] | wflags[5] | wflags[6] | wflags[7];
   const bool bad = flags != 0;
   lsum += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, lsum), 0x128, 0xf, 0xf, false));
   lsum = sum4rows(lsum);
