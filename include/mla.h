@@ -12,7 +12,9 @@
  *
  * and, upstream of step 2, the cache-append prolog mla_cache_append (RmsNorm
  * of the new latent rows, rope of their k_pe and of the query rope part, and
- * the slot-mapped write into the paged cache).
+ * the slot-mapped write into the paged cache).  For prefill and chunked
+ * prefill, mla_prefill_attention runs the naive (multi-head) form over the
+ * same paged cache.
  *
  * Pages this interface follows (cited by title and section):
  *   memra-engine 0.124.0 source page "mla.rs": MlaDims (geometry), MlaDims::scale,
@@ -215,8 +217,44 @@ mla_status mla_cache_append(const mla_dims* dims, int64_t n_tok, const void* c_k
                             int64_t num_blocks, int32_t block_size, uint32_t* data_err,
                             void* stream);
 
+/* Naive-form (multi-head) attention for prefill and chunked prefill over the
+ * paged latent cache (memra mla.rs, mla_attend_naive, and the MlaInputs causal
+ * rule).  For request b, new query i < t_q and head h, with L = seq_lens[b]
+ * counting every cache row of the request including its t_q new ones:
+ *   k_nope_j = W_UK[h] c_kv_j (d_nope wide),  v_j = W_UV[h] c_kv_j (d_v wide),
+ *   s_j = scale * (<q_nope[b][i][h], k_nope_j> + <q_pe[b][i][h], k_pe_j>),
+ *   out[b][i][h] = sum_j softmax(s)_j v_j  over rows j = 0 .. L - t_q + i,
+ *   lse[b][i][h] = natural log of sum_j exp(s_j);  L == 0: zeros and -inf.
+ * Rows are read through the block table as in mla_decode_attention.  The
+ * cache rows are first decompressed per head into the workspace (one GEMM
+ * per request), then attended at query-key width d_nope + d_rope.
+ * q_nope [batch][t_q][n_head][d_nope], q_pe [batch][t_q][n_head][d_rope] (NULL
+ * allowed when d_rope == 0), w_uk [n_head][d_nope][kv_rank], w_uv
+ * [n_head][d_v][kv_rank], kv_cache [num_blocks][block_size][kv_rank + d_rope]:
+ * all bfloat16.  out [batch][t_q][n_head][d_v] of type out_dt; lse float32
+ * [batch][t_q][n_head] or NULL.  workspace: at least
+ * mla_prefill_workspace_size() bytes for the same (dims, batch, max_blocks);
+ * it also holds the data-error word read by mla_decode_status.
+ * Supported geometry: kv_rank 512, d_v 256, d_nope + d_rope = 256 with d_rope
+ * 64 or 0, n_head * d_nope a multiple of 128 (GLM-5.2 and its NoPE variant).
+ * Errors: MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE (batch < 0, t_q < 1,
+ * max_blocks < 1, num_blocks < 1), MLA_ERR_UNSUPPORTED (block_size != 16,
+ * float32 inputs, another geometry), MLA_ERR_ARG (scale not finite or <= 0,
+ * bad dtype code), MLA_ERR_WORKSPACE, MLA_ERR_HIP.  Data errors found on the
+ * device (the MLA_DATA_* bits) do not fail the call: they poison that
+ * request's outputs with NaN and are reported by mla_decode_status. */
+mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_blocks,
+                                      int32_t block_size, size_t* bytes);
+mla_status mla_prefill_attention(const mla_dims* dims, float scale, int32_t batch, int32_t t_q,
+                                 const void* q_nope, const void* q_pe, const void* w_uk,
+                                 const void* w_uv, const void* kv_cache, mla_dtype dt,
+                                 int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* seq_lens, void* out,
+                                 mla_dtype out_dt, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Waits for `stream`, then ORs the MLA_DATA_* bits that the most recent
- * mla_decode_attention call on this workspace recorded into *flags (0 = no
+ * mla_decode_attention or mla_prefill_attention call on this workspace recorded into *flags (0 = no
  * data error).  Errors: MLA_ERR_NULL, MLA_ERR_WORKSPACE (the workspace holds
  * no completed decode), MLA_ERR_HIP. */
 mla_status mla_decode_status(const void* workspace, uint32_t* flags, void* stream);

@@ -197,6 +197,10 @@ SPECS = {
                       max_blocks=8192, seed=505, seq_len=131072),
     "nope_wide": Spec("nope_wide", 64, 256, 0, 256, 512, "bf16", batch=256, t_q=1,
                       max_blocks=64, seed=506, seq_len=1024),
+    # Chunked prefill on GLM-5.2 dims: 2 requests of 4096 rows whose last 1024
+    # are the new (causal) queries.
+    "glm52_prefill": Spec("glm52_prefill", 64, 192, 64, 256, 512, "bf16", batch=2, t_q=1024,
+                          max_blocks=256, seed=606, seq_len=4096),
 }
 
 

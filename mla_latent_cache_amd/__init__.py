@@ -5,8 +5,9 @@ The hot path is three library calls, each a hand-written HIP kernel set:
 attention over the paged latent cache plus the LSE-weighted merge) and
 ``mla_decompress_v`` (one W_UV decompression).  Upstream of attention,
 ``mla_cache_append`` writes the new tokens' RmsNorm'd and rope'd latent rows
-into the paged cache and rotates the query rope part.  See include/mla.h for
-the contract of every entry point.
+into the paged cache and rotates the query rope part; ``mla_prefill_attention``
+runs the naive (multi-head) form for prefill and chunked prefill.  See
+include/mla.h for the contract of every entry point.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
@@ -32,5 +33,7 @@ from ._binding import (  # noqa: F401
     mla_decompress_v,
     mla_default_scale,
     mla_dims,
+    mla_prefill_attention,
+    mla_prefill_workspace_size,
     mla_status_string,
 )

@@ -24,7 +24,8 @@ MLA_ROPE_NEOX, MLA_ROPE_INTERLEAVED = 0, 1
 
 EXPORTS = ("mla_default_scale", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode_resolve_splits", "mla_decode_attention", "mla_decompress_v",
-           "mla_decode_status", "mla_status_string", "mla_cache_append")
+           "mla_decode_status", "mla_status_string", "mla_cache_append", "mla_prefill_workspace_size",
+           "mla_prefill_attention")
 
 
 class MlaError(RuntimeError):
@@ -72,6 +73,11 @@ def lib():
     L.mla_cache_append.restype = ctypes.c_int
     L.mla_cache_append.argtypes = [P, i64, vp, vp, vp, ctypes.c_int, f32, vp, ctypes.c_double, i32, vp, vp,
                                    vp, ctypes.c_int, i64, i32, vp, vp]
+    L.mla_prefill_workspace_size.restype = ctypes.c_int
+    L.mla_prefill_workspace_size.argtypes = [P, i32, i32, i32, ctypes.POINTER(sz)]
+    L.mla_prefill_attention.restype = ctypes.c_int
+    L.mla_prefill_attention.argtypes = [P, f32, i32, i32, vp, vp, vp, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
+                                        vp, ctypes.c_int, vp, vp, sz, vp]
     L.mla_status_string.restype = ctypes.c_char_p
     L.mla_status_string.argtypes = [ctypes.c_int]
     _LIB = L
@@ -204,6 +210,34 @@ def mla_cache_append(dims: DimsLike, c_kv, k_pe, gamma, eps: float, positions, r
         ctypes.byref(d), n_tok, _ptr(c_kv), _ptr(pe), _ptr(gamma), _dt(c_kv), float(eps), _ptr(positions),
         float(rope_base), int(rope_style), _ptr(qpe), _ptr(slot_mapping), _ptr(kv_cache), _dt(kv_cache),
         int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(data_err), _stream(stream)))
+
+
+def mla_prefill_workspace_size(dims: DimsLike, batch: int, max_blocks: int, block_size: int = 16) -> int:
+    d = as_dims(dims)
+    out = ctypes.c_size_t(0)
+    _check("mla_prefill_workspace_size",
+           lib().mla_prefill_workspace_size(ctypes.byref(d), batch, max_blocks, block_size, ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_prefill_attention(dims: DimsLike, scale: float, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_lens,
+                          out, lse=None, workspace=None, stream=None) -> None:
+    """Naive-form prefill attention.  q_nope [B][t_q][H][d_nope], q_pe
+    [B][t_q][H][d_rope] or None, w_uk [H][d_nope][kv_rank], w_uv
+    [H][d_v][kv_rank], kv_cache [num_blocks][16][D], block_table int32
+    [B][max_blocks], seq_lens int32 [B], out [B][t_q][H][d_v], lse float32
+    [B][t_q][H] or None, workspace a uint8 device tensor of at least
+    mla_prefill_workspace_size() bytes."""
+    d = as_dims(dims)
+    B, t_q = int(q_nope.shape[0]), int(q_nope.shape[1])
+    if workspace is None:
+        raise ValueError("mla_prefill_attention needs a workspace tensor")
+    pe = q_pe if (q_pe is not None and q_pe.numel() > 0) else None
+    _check("mla_prefill_attention", lib().mla_prefill_attention(
+        ctypes.byref(d), float(scale), B, t_q, _ptr(q_nope), _ptr(pe), _ptr(w_uk), _ptr(w_uv), _ptr(kv_cache),
+        _dt(kv_cache), int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(block_table),
+        int(block_table.shape[1]), _ptr(seq_lens), _ptr(out), _dt(out), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def mla_status_string(code: int) -> str:

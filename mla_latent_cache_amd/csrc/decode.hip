@@ -89,23 +89,6 @@ __device__ __forceinline__ void write_header(const DecodeArgs& a) {
   }
 }
 
-// s_waitcnt with vmcnt <= N and no constraint on the other counters.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
-}
-
-// Workgroup barrier that keeps vector-memory loads in flight: it waits only
-// for this wave's LDS accesses, unlike __syncthreads(), whose release fence
-// also waits for every outstanding global load.  The empty asm statements
-// keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_keep_loads() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 
 constexpr float kSlack = 8.f;   // log2 headroom before the softmax reference moves

@@ -115,13 +115,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // offsets at or past the resource size deliver zeros.  Issued as inline assembly so the
 // compiler does not track it: the caller orders it with explicit vmcnt waits.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_wave_base, uint32_t voff) {
+  // The LDS base is wave-uniform; take it from the first lane so it is a scalar operand.
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_wave_base);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %1, %2, 0 offen lds"
       :
-      : "s"(lds_wave_base), "v"(voff), "s"(rsrc)
+      : "s"(base), "v"(voff), "s"(rsrc)
       : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt <= N and no constraint on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier that keeps vector-memory loads in flight: it waits only
+// for this wave's LDS accesses, unlike __syncthreads(), whose release fence
+// also waits for every outstanding global load.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows

@@ -85,4 +85,36 @@ struct CacheAppend {
 
 hipError_t launch_cache_append(const CacheAppend& c, hipStream_t stream);
 
+// One naive-form prefill call.  Workspace: the 256-byte header, one status
+// word per request, then K_nope [B][H][max_rows][d_nope] and V
+// [B][H][max_rows][d_v] (bf16), each 256-byte aligned.
+struct PrefillArgs {
+  const void* q_nope;        // [B][t_q][H][d_nope]
+  const void* q_pe;          // [B][t_q][H][d_rope]
+  const void* w_uk;          // [H][d_nope][kv_rank]
+  const void* w_uv;          // [H][d_v][kv_rank]
+  const void* kv;            // [num_blocks][16][kv_rank + d_rope]
+  const int32_t* bt;         // [B][max_blocks]
+  const int32_t* seq_lens;   // [B]
+  void* out;                 // [B][t_q][H][d_v]
+  float* lse;                // [B][t_q][H] or null
+  uint16_t* kw;              // workspace K_nope
+  uint16_t* vw;              // workspace V
+  uint32_t* header;          // workspace header
+  uint32_t* status;          // [B]
+  int64_t num_blocks;
+  int batch, t_q, n_head, max_blocks, max_rows;
+  float scale;
+  int out_bf16;
+};
+
+struct PrefillPlan {
+  int max_rows;
+  size_t status_off, kw_off, vw_off, bytes;
+};
+
+PrefillPlan prefill_plan(int n_head, int d_nope, int d_rope, int d_v, int kv_rank, int batch, int max_blocks);
+bool prefill_supported(int n_head, int d_nope, int d_rope, int d_v, int kv_rank);
+hipError_t launch_prefill(const PrefillArgs& a, int d_rope, hipStream_t stream);
+
 }  // namespace mla

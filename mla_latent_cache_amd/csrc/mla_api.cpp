@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include "kernels.hpp"
@@ -254,6 +255,67 @@ mla_status mla_cache_append(const mla_dims* dims, int64_t n_tok, const void* c_k
   c.interleaved = rope_style == MLA_ROPE_INTERLEAVED;
   const hipError_t e = mla::launch_cache_append(c, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidValue) return MLA_ERR_SHAPE;
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_prefill_workspace_size(const mla_dims* dims, int32_t batch, int32_t max_blocks, int32_t block_size,
+                                      size_t* bytes) {
+  if (!dims || !bytes) return MLA_ERR_NULL;
+  if (dims->n_head < 1 || dims->d_nope < 1 || dims->d_rope < 0 || dims->d_v < 1 || dims->kv_rank < 1)
+    return MLA_ERR_DIMS;
+  if (batch < 0 || max_blocks < 1) return MLA_ERR_SHAPE;
+  if (block_size != 16) return MLA_ERR_UNSUPPORTED;
+  if (!mla::prefill_supported(dims->n_head, dims->d_nope, dims->d_rope, dims->d_v, dims->kv_rank))
+    return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)max_blocks * 16 > INT32_MAX) return MLA_ERR_SHAPE;
+  *bytes = mla::prefill_plan(dims->n_head, dims->d_nope, dims->d_rope, dims->d_v, dims->kv_rank, batch, max_blocks)
+               .bytes;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_attention(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_nope,
+                                 const void* q_pe, const void* w_uk, const void* w_uv, const void* kv_cache,
+                                 mla_dtype dt, int64_t num_blocks, int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* seq_lens, void* out, mla_dtype out_dt, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const mla_status ws = mla_prefill_workspace_size(dims, batch, max_blocks, block_size, &need);
+  if (ws != MLA_OK) return ws;
+  if (t_q < 1 || num_blocks < 1) return MLA_ERR_SHAPE;
+  if (!dt_ok(dt) || !dt_ok(out_dt)) return MLA_ERR_ARG;
+  if (dt != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !isfinite(scale)) return MLA_ERR_ARG;
+  if (!workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !w_uv || !kv_cache || !block_table || !seq_lens || !out || (dims->d_rope > 0 && !q_pe))
+    return MLA_ERR_NULL;
+  const mla::PrefillPlan p = mla::prefill_plan(dims->n_head, dims->d_nope, dims->d_rope, dims->d_v, dims->kv_rank,
+                                               batch, max_blocks);
+  char* wsb = static_cast<char*>(workspace);
+  mla::PrefillArgs a = {};
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.kv = kv_cache;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.kw = reinterpret_cast<uint16_t*>(wsb + p.kw_off);
+  a.vw = reinterpret_cast<uint16_t*>(wsb + p.vw_off);
+  a.header = reinterpret_cast<uint32_t*>(wsb);
+  a.status = reinterpret_cast<uint32_t*>(wsb + p.status_off);
+  a.num_blocks = num_blocks;
+  a.batch = batch;
+  a.t_q = t_q;
+  a.n_head = dims->n_head;
+  a.max_blocks = max_blocks;
+  a.max_rows = p.max_rows;
+  a.scale = scale;
+  a.out_bf16 = out_dt == MLA_BF16;
+  const hipError_t e = mla::launch_prefill(a, dims->d_rope, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

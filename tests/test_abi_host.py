@@ -149,6 +149,50 @@ def test_cache_append_host_validation():
     assert append(dims=dims(nope), n_tok=0, k_pe=None, pos=None, base=0.0) == B.MLA_OK
 
 
+def prefill(**kw):
+    a = dict(dims=dims(), scale=0.0625, batch=2, t_q=4, qn=FAKE, qp=FAKE, wuk=FAKE, wuv=FAKE, kv=FAKE,
+             dt=B.MLA_BF16, num_blocks=10, block_size=16, bt=FAKE, max_blocks=4, sl=FAKE, out=FAKE,
+             out_dt=B.MLA_BF16, lse=None, ws=FAKE, ws_bytes=1 << 34, stream=None)
+    a.update(kw)
+    return mla.lib().mla_prefill_attention(a["dims"], a["scale"], a["batch"], a["t_q"], a["qn"], a["qp"], a["wuk"],
+                                           a["wuv"], a["kv"], a["dt"], a["num_blocks"], a["block_size"], a["bt"],
+                                           a["max_blocks"], a["sl"], a["out"], a["out_dt"], a["lse"], a["ws"],
+                                           a["ws_bytes"], a["stream"])
+
+
+def test_prefill_host_validation():
+    sz = ctypes.c_size_t()
+    L = mla.lib()
+    assert L.mla_prefill_workspace_size(dims(), 2, 4, 16, ctypes.byref(sz)) == B.MLA_OK
+    # header + status, then K_nope and V for 2 x 64 heads x 64 rows
+    assert sz.value >= 2 * 64 * 64 * (192 + 256) * 2
+    assert L.mla_prefill_workspace_size(dims((64, 256, 0, 256, 512)), 1, 8, 16, ctypes.byref(sz)) == B.MLA_OK
+    assert L.mla_prefill_workspace_size(dims((4, 16, 8, 16, 32)), 1, 8, 16, ctypes.byref(sz)) == B.MLA_ERR_UNSUPPORTED
+    assert L.mla_prefill_workspace_size(None, 1, 8, 16, ctypes.byref(sz)) == B.MLA_ERR_NULL
+    assert L.mla_prefill_workspace_size(dims(), -1, 8, 16, ctypes.byref(sz)) == B.MLA_ERR_SHAPE
+    assert L.mla_prefill_workspace_size(dims(), 1, 0, 16, ctypes.byref(sz)) == B.MLA_ERR_SHAPE
+    assert L.mla_prefill_workspace_size(dims(), 1, 8, 32, ctypes.byref(sz)) == B.MLA_ERR_UNSUPPORTED
+    assert prefill(dims=None) == B.MLA_ERR_NULL
+    assert prefill(dims=dims((0, 192, 64, 256, 512))) == B.MLA_ERR_DIMS
+    assert prefill(dims=dims((64, 128, 64, 256, 512))) == B.MLA_ERR_UNSUPPORTED   # qk width 192
+    assert prefill(dims=dims((64, 192, 64, 128, 512))) == B.MLA_ERR_UNSUPPORTED   # d_v 128
+    assert prefill(batch=-1) == B.MLA_ERR_SHAPE
+    assert prefill(t_q=0) == B.MLA_ERR_SHAPE
+    assert prefill(num_blocks=0) == B.MLA_ERR_SHAPE
+    assert prefill(block_size=8) == B.MLA_ERR_UNSUPPORTED
+    assert prefill(dt=B.MLA_F32) == B.MLA_ERR_UNSUPPORTED
+    assert prefill(dt=3) == B.MLA_ERR_ARG
+    assert prefill(scale=0.0) == B.MLA_ERR_ARG
+    assert prefill(scale=math.nan) == B.MLA_ERR_ARG
+    assert prefill(ws=None) == B.MLA_ERR_NULL
+    assert prefill(ws_bytes=1024) == B.MLA_ERR_WORKSPACE
+    assert prefill(qn=None) == B.MLA_ERR_NULL
+    assert prefill(qp=None) == B.MLA_ERR_NULL   # rope part needed
+    assert prefill(kv=None) == B.MLA_ERR_NULL
+    assert prefill(out=None) == B.MLA_ERR_NULL
+    assert prefill(batch=0, qn=None, qp=None, kv=None, out=None) == B.MLA_OK
+
+
 def test_default_scale_and_strings():
     assert mla.mla_default_scale(GLM52) == pytest.approx(1 / 16, abs=1e-9)
     assert mla.mla_default_scale((64, 256, 0, 256, 512)) == pytest.approx(1 / 16, abs=1e-9)
