@@ -206,6 +206,83 @@ def time_prolog(spec, case, dims, kv, stream, reps: int = 20, chunk: int = 4096)
     }
 
 
+def prefill_figures(spec, seq_lens):
+    """Algorithmic work of one naive-form prefill call: flops of the
+    decompression GEMM (every cache row of a request through W_UK and W_UV)
+    and of causal attention (query i of request b sees L_b - t_q + i + 1
+    rows; q.k at width d_nope + d_rope, p.v at width d_v), and the bytes the
+    call must move (cache rows, queries, weights, output, LSE).  The per-head
+    K/V the first kernel writes for the second is not counted."""
+    lens = [int(x) for x in seq_lens]
+    H, T, e = spec.n_head, spec.t_q, 2
+    vis = sum(sum(L - T + i + 1 for i in range(T)) for L in lens if L >= T)
+    att = vis * H * 2 * (spec.d_nope + spec.d_rope + spec.d_v)
+    dec = sum(max(L, 0) for L in lens) * H * (spec.d_nope + spec.d_v) * spec.kv_rank * 2
+    n_q = len(lens) * T * H
+    byts = (sum(max(L, 0) for L in lens) * spec.D * e + n_q * (spec.d_nope + spec.d_rope) * e
+            + H * (spec.d_nope + spec.d_v) * spec.kv_rank * e + n_q * spec.d_v * e + n_q * 4)
+    return {"attend_flops": att, "decompress_flops": dec, "bytes": byts}
+
+
+def time_prefill(name: str = "glm52_prefill", reps: int = 10):
+    """The naive-form prefill call (decompression GEMM + causal flash
+    attention) timed on its own with HIP events on its stream."""
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_latent_cache_amd as mla
+
+    spec = mi.SPECS[name]
+    case = mi.make_case(spec)
+    B, T, H = spec.batch, spec.t_q, spec.n_head
+    dims = (spec.n_head, spec.d_nope, spec.d_rope, spec.d_v, spec.kv_rank)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    qn = dev(case.q_nope).view(B, T, H, spec.d_nope)
+    qp = dev(case.q_pe).view(B, T, H, spec.d_rope) if spec.d_rope else None
+    wuk, wuv, kv = dev(case.w_uk), dev(case.w_uv), dev(case.kv)
+    bt = torch.from_numpy(case.block_table).cuda()
+    sl = torch.from_numpy(case.seq_lens).cuda()
+    out = torch.empty(B, T, H, spec.d_v, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.mla_prefill_workspace_size(dims, B, spec.max_blocks), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        mla.mla_prefill_attention(dims, case.scale, qn, qp, wuk, wuv, kv, bt, sl, out, lse, ws, stream)
+
+    for _ in range(3):
+        call()
+    if mla.mla_decode_status(ws, stream) != 0:
+        raise RuntimeError("prefill benchmark: the call reported a data error")
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in es:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in es) / reps * 1e-3  # seconds
+    f = prefill_figures(spec, case.seq_lens)
+    flops = f["attend_flops"] + f["decompress_flops"]
+    tflops = flops / t / 1e12
+    return {
+        "kernels": "prefill_decompress (per-head K_nope/V GEMM) + prefill_attend (causal flash attention)",
+        "workload": f"{spec.name}: {H} heads, d_nope {spec.d_nope}, d_rope {spec.d_rope}, d_v {spec.d_v}, "
+                    f"kv_rank {spec.kv_rank}, batch {B} x {int(case.seq_lens[0])} rows, t_q {T} new queries",
+        "call_us": round(t * 1e6, 1),
+        "attend_flops": f["attend_flops"],
+        "decompress_flops": f["decompress_flops"],
+        "algorithmic_bytes": f["bytes"],
+        "bound": "mfma",
+        "tflops": round(tflops, 1),
+        "peak_tflops": BF16_PEAK_TFLOPS,
+        "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +293,7 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0, help="KV splits per request (0 = automatic)")
     ap.add_argument("--cpu-items", type=int, default=4096, help="oracle items for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the naive-form prefill measurement")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel of a timed step from the host instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -352,6 +430,7 @@ def main() -> int:
 
     prolog = time_prolog(spec, case, dims, copies[0]["kv"], stream)
     stage["cache_append"] = prolog["decode_step_us"] * 1e-3
+    prefill = None if args.no_prefill else time_prefill()
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -390,6 +469,7 @@ def main() -> int:
         "step_launch": "host launches" if args.eager else "HIP graph replay (absorb, split, merge, decompress)",
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "prolog": prolog,
+        "prefill": prefill,
         "roofline": {
             "kernel": "decode call: decode_split_mfma + decode_merge",
             "bound": "hbm",
