@@ -106,6 +106,10 @@ struct PrefillArgs {
   int batch, t_q, n_head, max_blocks, max_rows;
   float scale;
   int out_bf16;
+  // Launch geometry, filled by launch_prefill.
+  int n_wtiles;  // 128-row tiles of the stacked [W_UK; W_UV]
+  int n_mtiles;  // 128-row tiles of a request's cache rows
+  int wgroup;    // weight tiles one XCD keeps in L2 while the cache tiles stream
 };
 
 struct PrefillPlan {

@@ -66,6 +66,7 @@ __device__ __forceinline__ int row_swizzle(int r) {
 // ---------------------------------------------------------------------------
 constexpr int kGN = 128, kGM = 128, kGK = 64;  // weight rows, cache rows, k per chunk
 constexpr int kGChunks = kGK / 8;              // 16-byte chunks per staged row (8)
+constexpr int kWeightGroup = 14;               // weight tiles per XCD group (1.75 MB of bf16)
 
 template <int DR>
 __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a) {
@@ -74,8 +75,18 @@ __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a
   __shared__ __attribute__((aligned(16))) u32x4 sw[2][kGN * kGChunks];  // weight rows [128][64]
   __shared__ __attribute__((aligned(16))) u32x4 sc[2][kGM * kGChunks];  // cache rows [128][64]
 
-  const int b = blockIdx.z;
-  const int m0 = blockIdx.y * kGM, n0 = blockIdx.x * kGN;
+  // Workgroup i runs on XCD i % 8.  Each XCD takes whole groups of
+  // a.wgroup weight tiles (group g on XCD g % 8) and, per group, walks every
+  // cache-row tile with the group's weight tiles innermost, so the group's
+  // weights stay in that XCD's L2 while the cache tiles stream past.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per_group = a.batch * a.n_mtiles * a.wgroup;
+  const int grp = (slot / per_group) * 8 + xcd;
+  const int rem = slot - (slot / per_group) * per_group;
+  const int ct = rem / a.wgroup, wt = grp * a.wgroup + (rem - ct * a.wgroup);
+  if (wt >= a.n_wtiles) return;  // whole workgroup
+  const int b = ct / a.n_mtiles;
+  const int m0 = (ct - b * a.n_mtiles) * kGM, n0 = wt * kGN;
   const int64_t L = a.seq_lens[b];
   if (prefill_flags(L, a.t_q, a.max_blocks) != 0 || (int64_t)m0 >= L) return;  // whole workgroup
   const int rows = L - m0 < kGM ? (int)(L - m0) : kGM;
@@ -183,30 +194,84 @@ __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a
 // ---------------------------------------------------------------------------
 // Causal flash attention over the decompressed rows
 // ---------------------------------------------------------------------------
-constexpr int kAQ = 128;  // queries per workgroup (32 per wave)
-constexpr int kAT = 32;   // cache rows per tile
+constexpr int kAQ = 128;     // queries per workgroup (32 per wave)
+constexpr int kAT = 32;      // cache rows per tile
+constexpr int kAStages = 4;  // tile ring: three tiles in flight while one is used
 
 template <int DR>
 struct ATile {
   using G = PGeom<DR>;
   static constexpr int DN = G::DN, DV = G::DV;
-  static constexpr int KN_CH = DN / 8, KP_CH = DR / 8, V_CH = DV / 8;  // 16-byte chunks per row
-  static constexpr int KN = kAT * KN_CH, KP = kAT * KP_CH, VV = kAT * V_CH;  // chunks per tile
-  static constexpr int STAGE = KN + KP + VV;                                    // chunks per stage
-  static constexpr int LOADS = STAGE / 64;                                      // 1 KB loads per stage
-  static_assert(KN % 64 == 0 && KP % 64 == 0 && VV % 64 == 0 && LOADS % 4 == 0, "whole loads per wave");
-  static constexpr int KSTEPS = (DN + DR) / 32;
+  static constexpr int KN_CH = DN / 8, KP_CH = DR / 8, V_CH = DV / 8;  // 16-byte chunks of data per row
+  // Staged rows.  K_nope and k_pe rows keep their width, with the 16-byte
+  // chunks of row r permuted by an XOR with row_swizzle(r); V rows take two
+  // pad chunks (34 chunks = 544 bytes, a 32-byte bank shift per row).  Both
+  // keep the operand reads free of bank conflicts (measured), and both leave
+  // every operand address a lane base plus a constant: the XOR only touches
+  // the low 3 (K_nope at 24 chunks, k_pe) or 4 (K_nope at 32 chunks) chunk
+  // bits, so each residue of the k-step modulo KB gets a base of its own.
+  // V's pad chunks are filled with zeros and never read.
+  static constexpr int KN_P = KN_CH, KP_P = KP_CH, V_P = V_CH + 2;
+  static constexpr int KB = KN_CH % 16 == 0 ? 4 : 2;          // K_nope lane bases (k-steps per swizzle group)
+  static constexpr int KN_LOADS = (kAT * KN_P + 63) / 64;    // 1 KB loads of the K_nope rows
+  static constexpr int KP_HALF = (16 * KP_P + 63) / 64;       // loads per 16-row block of k_pe
+  static constexpr int KP_LOADS = DR > 0 ? 2 * KP_HALF : 0;
+  static constexpr int V_LOADS = (kAT * V_P + 63) / 64;
+  static constexpr int USED = KN_LOADS + KP_LOADS + V_LOADS;
+  static constexpr int LOADS = (USED + 3) / 4 * 4;            // every wave issues LPW loads
+  static constexpr int LPW = LOADS / 4;
+  static constexpr int STAGE = LOADS * 64;                     // chunks per stage
+  static constexpr int KP0 = KN_LOADS * 64, V0 = (KN_LOADS + KP_LOADS) * 64;  // region starts (chunks)
+  static constexpr int KSTEPS = (DN + DR) / 32, KN_STEPS = DN / 32;
+  static_assert(DN % 32 == 0 && DR % 32 == 0, "k-steps of 32 dims");
+  // Region boundaries on multiples of four loads: the j-th load of every
+  // wave lies in one region, known at compile time.
+  static_assert(KN_LOADS % 4 == 0 && KP_LOADS % 4 == 0 && KP_LOADS <= 4, "regions in whole load rounds");
+  static constexpr int region(int j) { return 4 * j < KN_LOADS ? 0 : (4 * j < KN_LOADS + KP_LOADS ? 1 : 2); }
+  static_assert(16 * (V0 + 16 * V_P) + 32 * (DV / 16) < 65536, "LDS offsets fit the instruction");
 };
+
+// LDS operand reads with a constant offset; the result is not ready until a
+// matching lgkm_wait (the compiler does not track these).
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128(uint32_t addr, u32x4& v) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr(uint32_t addr, uint2& v) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+}
+// Wait until at most N (< 16) LDS operations of this wave are outstanding;
+// the registers are tied to the wait so their uses cannot move above it.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& v) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "i"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(uint2& x, uint2& y) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N) : "memory");
+}
 
 template <int DR>
 __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
   using T = ATile<DR>;
   using G = PGeom<DR>;
   constexpr int DN = T::DN, DV = T::DV, D = G::D;
-  __shared__ __attribute__((aligned(16))) u32x4 stage[2][T::STAGE];
+  __shared__ __attribute__((aligned(16))) u32x4 stage[kAStages][T::STAGE];
   __shared__ uint32_t wflags[4];
 
-  const int b = blockIdx.z, h = blockIdx.y, i0 = blockIdx.x * kAQ;
+  // Workgroup i runs on XCD i % 8: the query tiles of one (request, head)
+  // take consecutive slots of one XCD, so they stream the same decompressed
+  // rows through one L2 at about the same time; the tiles that see the most
+  // rows go first.
+  const int n_qt = (a.t_q + kAQ - 1) / kAQ;
+  const int slot = blockIdx.x >> 3;
+  const int pair = (slot / n_qt) * 8 + (blockIdx.x & 7);
+  if (pair >= a.batch * a.n_head) return;  // whole workgroup
+  const int b = pair / a.n_head, h = pair - b * a.n_head;
+  const int i0 = (n_qt - 1 - (slot - (slot / n_qt) * n_qt)) * kAQ;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -242,61 +307,70 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
     }
   }
 
-  // Tile loads.  Stage layout (16-byte chunks): K_nope rows [0, KN), k_pe rows
-  // [KN, KN + KP), V rows [KN + KP, STAGE).  Load u (of LOADS) covers chunks
-  // [64 u, 64 u + 64); wave w issues loads u = w + 4 j.
+  // Tile loads.  Load u of a stage fills chunks [64 u, 64 u + 64): loads
+  // [0, KN_LOADS) the K_nope rows (pitch KN_P), then KP_HALF loads per 16-row
+  // block of k_pe (pitch KP_P), then the V rows (pitch V_P).  Wave w issues
+  // loads u = w + 4 j; the lane offsets do not depend on the tile.
   const uint16_t* kw = a.kw + ((int64_t)b * H + h) * a.max_rows * DN;
   const uint16_t* vw = a.vw + ((int64_t)b * H + h) * a.max_rows * DV;
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
+  constexpr uint32_t kOut = 0x40000000u;  // beyond any buffer range: loads zeros
+  uint32_t voffs[T::LPW];
+#pragma unroll
+  for (int j = 0; j < T::LPW; ++j) {
+    const int u = w + 4 * j, q = 64 * u + lane;
+    uint32_t v = kOut;
+    if (u < T::KN_LOADS) {
+      const int r = q / T::KN_P, p = q - r * T::KN_P;  // slot p of row r holds chunk p ^ swizzle(r)
+      if (r < kAT) v = (uint32_t)(r * DN * 2 + (p ^ row_swizzle<T::KN_CH>(r)) * 16);
+    } else if (u < T::KN_LOADS + T::KP_LOADS) {
+      const int ql = q - T::KP0 - ((u - T::KN_LOADS) / T::KP_HALF) * T::KP_HALF * 64;
+      const int r = ql / T::KP_P, p = ql - r * T::KP_P;
+      if (r < 16) v = (uint32_t)(r * D * 2 + (p ^ row_swizzle<T::KP_CH>(r)) * 16);
+    } else if (u < T::USED) {
+      const int qv = q - T::V0;
+      const int r = qv / T::V_P, p = qv - r * T::V_P;
+      if (r < kAT && p < T::V_CH) v = (uint32_t)(r * DV * 2 + p * 16);
+    }
+    voffs[j] = v;
+  }
   // Block ids through scalar loads (the table is read-only for the call), so
   // the vector-memory counter only tracks tile loads.
   typedef __attribute__((address_space(4))) const int32_t const_i32;
   const_i32* bt_s = (const_i32*)(a.bt + (int64_t)b * a.max_blocks);
   const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
-  auto issue_tile = [&](int t, int buf) {
+  // Block ids of tile t (scalar loads), -1 where the tile has no rows there.
+  auto load_ids = [&](int t, int32_t (&id)[2]) {
+    id[0] = id[1] = -1;
+    if constexpr (DR > 0) {
+      const int j0 = t * kAT;
+      id[0] = bt_s[j0 >> 4];
+      if (L - j0 > 16) id[1] = bt_s[(j0 >> 4) + 1];
+    }
+  };
+  auto issue_tile = [&](int t, int buf, const int32_t (&id)[2]) {
     const int j0 = t * kAT;
     const int nval = L - j0 >= kAT ? kAT : (int)(L - j0);  // rows that exist (>= 1)
     const i32x4 rs_k = raw_rsrc(kw + (int64_t)j0 * DN, (uint32_t)(nval * DN * 2));
     const i32x4 rs_v = raw_rsrc(vw + (int64_t)j0 * DV, (uint32_t)(nval * DV * 2));
-    i32x4 rs_p[2];
+    i32x4 rs_p = rs_v;
     if constexpr (DR > 0) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int nv = nval - 16 * hb <= 0 ? 0 : (nval - 16 * hb >= 16 ? 16 : nval - 16 * hb);
-        int32_t id = -1;
-        if (nv > 0) id = bt_s[(j0 >> 4) + hb];
-        const bool ok = (uint32_t)id < nb32;
-        if (nv > 0 && !ok) flags |= kBadBlock;
-        // k_pe of row r of the block at byte r * D * 2 from the block's column 512
-        rs_p[hb] = raw_rsrc(kv + (int64_t)(ok ? id : 0) * (16 * D) + G::KR,
-                            ok && nv > 0 ? (uint32_t)((nv - 1) * D * 2 + DR * 2) : 0u);
-      }
+      // k_pe of this wave's block (the fourth load round: wave w takes block
+      // w / KP_HALF); row r of a block at byte r * D * 2 from its column 512.
+      const int hb = w / T::KP_HALF;
+      const int nv = nval - 16 * hb <= 0 ? 0 : (nval - 16 * hb >= 16 ? 16 : nval - 16 * hb);
+      const int32_t bid = hb ? id[1] : id[0];
+      const bool ok = (uint32_t)bid < nb32;
+      // every wave checks both blocks, so each wave's flags see every bad id
+      if ((uint32_t)id[0] >= nb32 || (nval > 16 && (uint32_t)id[1] >= nb32)) flags |= kBadBlock;
+      rs_p = raw_rsrc(kv + (int64_t)(ok ? bid : 0) * (16 * D) + G::KR,
+                      ok && nv > 0 ? (uint32_t)((nv - 1) * D * 2 + DR * 2) : 0u);
     }
     const uint32_t base = lds_addr(stage[buf]);
 #pragma unroll
-    for (int j = 0; j < T::LOADS / 4; ++j) {
-      const int u = w + 4 * j;
-      const int unit = 64 * u + lane;  // chunk of the stage
-      uint32_t voff;
-      if (u * 64 < T::KN) {
-        const int r = unit / T::KN_CH, p = unit - r * T::KN_CH;
-        voff = (uint32_t)(r * DN * 2 + (p ^ row_swizzle<T::KN_CH>(r)) * 16);
-        dma16(rs_k, base + 1024u * u, voff);
-      } else if (DR > 0 && u * 64 < T::KN + T::KP) {
-        if constexpr (DR > 0) {
-          const int pu = unit - T::KN;
-          const int r = pu / T::KP_CH, p = pu - r * T::KP_CH;
-          voff = (uint32_t)((r & 15) * D * 2 + (p ^ row_swizzle<T::KP_CH>(r)) * 16);
-          // the 8 rows of one load lie in one block
-          const int blk = ((u * 64 - T::KN) / T::KP_CH) >> 4;
-          dma16(blk ? rs_p[1] : rs_p[0], base + 1024u * u, voff);
-        }
-      } else {
-        const int vu = unit - T::KN - T::KP;
-        const int r = vu / T::V_CH, p = vu - r * T::V_CH;
-        voff = (uint32_t)(r * DV * 2 + (p ^ (2 * (r & 7))) * 16);
-        dma16(rs_v, base + 1024u * u, voff);
-      }
+    for (int j = 0; j < T::LPW; ++j) {
+      const i32x4 rs = T::region(j) == 0 ? rs_k : (T::region(j) == 1 ? rs_p : rs_v);
+      dma16(rs, base + 1024u * (uint32_t)(w + 4 * j), voffs[j]);
     }
   };
 
@@ -309,98 +383,166 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) horizon[n] = qi[n] < t_q ? (int)(L - t_q + qi[n]) : -1;
 
-  // K operand (A of S^T): row 16 kt + l16 of the tile, dims 32 ks + 8 g.
-  auto k_frag = [&](const char* st, int kt, int ks) {
-    const int r = 16 * kt + l16;
-    const int ch = 4 * ks + g;
-    if (32 * ks < DN) {
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(st + (r * T::KN_CH + (ch ^ row_swizzle<T::KN_CH>(r))) * 16));
-    } else {
-      const int cp = ch - T::KN_CH;
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(st + (T::KN + r * T::KP_CH + (cp ^ row_swizzle<T::KP_CH>(r))) * 16));
-    }
-  };
-  // V^T (A of O^T) for value columns 16 dt .. + 15: tile rows 4 g + e and
-  // 16 + 4 g + e (the lane's k slots), read transposed.  Provider lane a of a
-  // 16-lane group gives row 4 g + a / 4 (+ 16), columns 16 dt + 4 (a % 4).
+  // Lane bases of the operand reads within a stage (bytes).
+  //   K (A of S^T), rows 16 kt + l16, dims 32 ks + 8 g: K_nope for
+  //   ks < KN_STEPS, then k_pe (block kt).
+  //   V^T (A of O^T) for columns 16 dt .. + 15: tile rows 4 g + e and
+  //   16 + 4 g + e (the lane's k slots), read transposed.  Provider lane a of
+  //   a 16-lane group gives row 4 g + a / 4 (+ 16), columns 16 dt + 4 (a % 4).
+  //   Rows 16 kt + l16 share l16's swizzle, so kt is a constant offset.
+  uint32_t bk[T::KB], bp[2];
+#pragma unroll
+  for (int q = 0; q < T::KB; ++q) bk[q] = 16u * (uint32_t)(l16 * T::KN_P + ((4 * q + g) ^ row_swizzle<T::KN_CH>(l16)));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) bp[q] = DR > 0 ? 16u * (uint32_t)(l16 * T::KP_P + ((4 * q + g) ^ row_swizzle<8>(l16))) : 0u;
   const int vr = 4 * g + (l16 >> 2);
-  auto v_frag = [&](const char* st, int dt) {
-    const char* vb = st + (T::KN + T::KP) * 16;
-    const int c = 2 * dt + ((l16 & 3) >> 1);  // chunk of columns 16 dt + 4 (l16 % 4)
-    const s16x4 v0 = lds_read_tr16(vb + (vr * T::V_CH + (c ^ (2 * (vr & 7)))) * 16 + (l16 & 1) * 8);
-    const int vr1 = vr + 16;
-    const s16x4 v1 = lds_read_tr16(vb + (vr1 * T::V_CH + (c ^ (2 * (vr1 & 7)))) * 16 + (l16 & 1) * 8);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
+  const uint32_t bv = 16u * (uint32_t)(vr * T::V_P + ((l16 & 3) >> 1)) + 8u * (uint32_t)(l16 & 1);
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    wait_vmcnt<0>();       // this wave's loads of tile t are done
-    barrier_keep_loads();  // tile t visible; every wave is past tile t - 1
-    // Buffer buf ^ 1 held tile t - 1, which no wave reads any more.
-    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);
-    const char* st = reinterpret_cast<const char*>(stage[buf]);
-
-    // S^T for the tile's two 16-row halves and this wave's two query tiles.
-    f32x4 sp[2][2];
+  // S^T of one tile into sp: the 2 x KSTEPS (k-step, row half) reads run kA
+  // steps ahead of the MFMAs, with exact waits.
+  constexpr int NS = 2 * T::KSTEPS, kA = 8;
+  static_assert(NS > kA && kA < 16, "read-ahead must fit the LDS counter");
+  // The S step I also runs piece I of the caller's work (the softmax of the
+  // previous tile), so that the vector ALU works while the matrix cores do.
+  auto s_tile = [&](uint32_t sb, f32x4 (&sp)[2][2], auto&& piece) {
+    u32x4 kr[NS];
+    auto rd = [&]<int I>() {
+      constexpr int ks = I / 2, kt = I % 2;
+      if constexpr (ks < T::KN_STEPS)
+        lds_read_b128<16 * 16 * T::KN_P * kt + 16 * 4 * T::KB * (ks / T::KB)>(sb + bk[ks % T::KB], kr[I]);
+      else
+        lds_read_b128<16 * (T::KP0 + kt * T::KP_HALF * 64)>(sb + bp[ks - T::KN_STEPS], kr[I]);
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) { (rd.template operator()<I>(), ...); }(
+        std::make_integer_sequence<int, kA>{});
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) sp[kt][0] = sp[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < T::KSTEPS; ++ks) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 kA = k_frag(st, kt, ks);
-        sp[kt][0] = mfma16x16x32(kA, qf[0][ks], sp[kt][0]);
-        sp[kt][1] = mfma16x16x32(kA, qf[1][ks], sp[kt][1]);
-      }
-      // bound how far operand reads are hoisted (register budget of two waves per SIMD)
-      if (ks % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (([&] {
+         constexpr int ks = I / 2, kt = I % 2;
+         constexpr int issued = I + kA < NS ? I + kA : NS;
+         lgkm_wait<issued - 1 - I>(kr[I]);
+         const bf16x8 kA_ = as_bf16x8(kr[I]);
+         sp[kt][0] = mfma16x16x32(kA_, qf[0][ks], sp[kt][0]);
+         sp[kt][1] = mfma16x16x32(kA_, qf[1][ks], sp[kt][1]);
+         if constexpr (I + kA < NS) rd.template operator()<I + kA>();
+         piece.template operator()<I>();
+         __builtin_amdgcn_sched_barrier(0);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, NS>{});
+  };
+  auto no_piece = []<int I>() {};
 
-    // Online softmax per query (lane column), rows 16 kt + 4 g + i.
-    bf16x8 pB[2];
-    float alpha[2];
+  // Software pipeline, one wave per SIMD: the S products of tile t + 1 are
+  // independent of the softmax and PV products of tile t.  Ring of kAStages
+  // tiles: t (V read by PV), t + 1 (K read by S), t + 2 in flight, t + 3
+  // issued into the buffer tile t - 1 released.
+  constexpr int LPW = T::LPW;
+  constexpr int ND = DV / 16, kAV = 6;  // PV column tiles; reads (two each) run kAV tiles ahead
+  static_assert(ND > kAV && 2 * kAV < 16, "read-ahead must fit the LDS counter");
+  int32_t nid[2];  // block ids of the next tile to issue, loaded one iteration ahead
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float tmax = -INFINITY;
-      float sc[2][4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = t * kAT + 16 * kt + 4 * g + i;
-          sc[kt][i] = j <= horizon[n] ? sp[kt][n][i] * sl2 : -INFINITY;
-          tmax = fmaxf(tmax, sc[kt][i]);
-        }
-      tmax = max4rows(tmax);
-      const bool grow = tmax > m2[n] + kSlackP;
-      alpha[n] = grow && m2[n] > -INFINITY ? __builtin_amdgcn_exp2f(m2[n] - tmax) : 1.f;
-      if (grow) m2[n] = tmax;
-      const float m_use = m2[n] == -INFINITY ? 0.f : m2[n];
-      float p[2][4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[kt][i] = __builtin_amdgcn_exp2f(sc[kt][i] - m_use);
-      lsum[n] = lsum[n] * alpha[n] + (((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3])));
-      pB[n] = as_bf16x8(u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                              pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
+  for (int k = 0; k < kAStages - 1; ++k)
+    if (k < n_tiles) {
+      load_ids(k, nid);
+      issue_tile(k, k, nid);
     }
-    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
+  if (kAStages - 1 < n_tiles) load_ids(kAStages - 1, nid);
+  f32x4 spc[2][2];  // raw scores of the current tile
+  if (n_tiles > 0) {
+    if (n_tiles >= 3) wait_vmcnt<2 * LPW>();
+    else if (n_tiles == 2) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    barrier_keep_loads();  // tile 0 visible
+    s_tile(lds_addr(stage[0]), spc, no_piece);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    // Tile t + 1 resident: at most the loads of tile t + 2 still outstanding.
+    if (t + 2 < n_tiles) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    barrier_keep_loads();  // tile t + 1 visible; every wave is past PV of tile t - 1
+    if (t + kAStages - 1 < n_tiles) issue_tile(t + kAStages - 1, (t + kAStages - 1) % kAStages, nid);
+
+    // Online softmax of tile t per query (lane column): element e = 4 kt + i
+    // is row 16 kt + 4 g + i of the tile.  Sixteen pieces, one per S step:
+    // for query tile n = I / 8, pieces 0-3 scale and mask two elements each
+    // and keep a running maximum, piece 4 takes the maximum over the four
+    // lane rows and moves the reference (delayed by kSlackP), pieces 5-7 form
+    // the probabilities, their sum and the packed P^T operand.
+    int lim[2];  // element e of query tile n is visible when 16 kt + i <= lim[n]
 #pragma unroll
-      for (int c = 0; c < DV / 16; ++c) {
+    for (int n = 0; n < 2; ++n) lim[n] = horizon[n] - t * kAT - 4 * g;
+    float sc[2][8], tmx[2], alpha[2], m_use[2], pr[2][8];
+    bf16x8 pB[2];
+    auto sm_piece = [&]<int I>() {
+      constexpr int n = I / 8, k = I % 8;
+      if constexpr (k < 4) {
+#pragma unroll
+        for (int e = 2 * k; e < 2 * k + 2; ++e) {
+          sc[n][e] = 16 * (e / 4) + (e % 4) <= lim[n] ? spc[e / 4][n][e % 4] * sl2 : -INFINITY;
+          tmx[n] = e == 0 ? sc[n][0] : fmaxf(tmx[n], sc[n][e]);
+        }
+      } else if constexpr (k == 4) {
+        const float tm = max4rows(tmx[n]);
+        const bool grow = tm > m2[n] + kSlackP;
+        alpha[n] = grow && m2[n] > -INFINITY ? __builtin_amdgcn_exp2f(m2[n] - tm) : 1.f;
+        if (grow) m2[n] = tm;
+        m_use[n] = m2[n] == -INFINITY ? 0.f : m2[n];
+      } else {
+        constexpr int e0 = k == 5 ? 0 : (k == 6 ? 3 : 6), e1 = k == 5 ? 3 : (k == 6 ? 6 : 8);
+#pragma unroll
+        for (int e = e0; e < e1; ++e) {
+          pr[n][e] = __builtin_amdgcn_exp2f(sc[n][e] - m_use[n]);
+          asm volatile("" : "+v"(pr[n][e]));  // computed here, not sunk to its use after a branch
+        }
+        if constexpr (k == 7) {
+          const float* q = pr[n];
+          lsum[n] = lsum[n] * alpha[n] + (((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7])));
+          u32x4 pk = {pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]), pack_bf16x2(q[4], q[5]), pack_bf16x2(q[6], q[7])};
+          asm volatile("" : "+v"(pk), "+v"(lsum[n]));
+          pB[n] = as_bf16x8(pk);
+        }
+      }
+    };
+
+    // S of tile t + 1 beside the softmax of tile t (on the last tile the S
+    // products read a stale buffer that no load targets; they are not used).
+    f32x4 spn[2][2];
+    s_tile(lds_addr(stage[(t + 1) % kAStages]), spn, sm_piece);
+    // The ids of the tile issued next iteration; the next barrier's wait
+    // covers their latency.
+    if (t + kAStages < n_tiles) load_ids(t + kAStages, nid);
+
+    const uint32_t vb = lds_addr(stage[t % kAStages]) + bv;
+    uint2 vv[ND][2];
+    auto rdv = [&]<int DT>() {
+      lds_read_tr<16 * T::V0 + 32 * DT>(vb, vv[DT][0]);
+      lds_read_tr<16 * (T::V0 + 16 * T::V_P) + 32 * DT>(vb, vv[DT][1]);
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) { (rdv.template operator()<I>(), ...); }(
+        std::make_integer_sequence<int, kAV>{});
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {  // rare, uniform
+#pragma unroll
+      for (int c = 0; c < ND; ++c) {
         acc[c][0] *= alpha[0];
         acc[c][1] *= alpha[1];
       }
     }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (([&] {
+         constexpr int issued = I + kAV < ND ? I + kAV : ND;
+         lgkm_wait<2 * (issued - 1 - I)>(vv[I][0], vv[I][1]);
+         const bf16x8 vA = __builtin_bit_cast(bf16x8, u32x4{vv[I][0].x, vv[I][0].y, vv[I][1].x, vv[I][1].y});
+         acc[I][0] = mfma16x16x32(vA, pB[0], acc[I][0]);
+         acc[I][1] = mfma16x16x32(vA, pB[1], acc[I][1]);
+         if constexpr (I + kAV < ND) rdv.template operator()<I + kAV>();
+         __builtin_amdgcn_sched_barrier(0);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, ND>{});
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      const bf16x8 vA = v_frag(st, dt);
-      acc[dt][0] = mfma16x16x32(vA, pB[0], acc[dt][0]);
-      acc[dt][1] = mfma16x16x32(vA, pB[1], acc[dt][1]);
-      if (dt % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int kt = 0; kt < 2; ++kt) spc[kt][0] = spn[kt][0], spc[kt][1] = spn[kt][1];
   }
 
   // Block-id errors are seen by the waves that issued the loads: share them.
@@ -470,15 +612,21 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_rope, hipStream_t stream) 
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.batch == 0 || a.t_q == 0) return e;
+  PrefillArgs g = a;
   const int n_cols = a.n_head * ((d_rope == 64 ? 192 : 256) + 256);
-  const dim3 g1(n_cols / kGN, (a.max_rows + kGM - 1) / kGM, a.batch);
-  const dim3 g2((a.t_q + kAQ - 1) / kAQ, a.n_head, a.batch);
+  g.n_wtiles = n_cols / kGN;
+  g.n_mtiles = (a.max_rows + kGM - 1) / kGM;
+  g.wgroup = g.n_wtiles < kWeightGroup ? g.n_wtiles : kWeightGroup;
+  const int64_t groups = (g.n_wtiles + g.wgroup - 1) / g.wgroup;
+  const int64_t n1 = 8 * ((groups + 7) / 8) * (int64_t)a.batch * g.n_mtiles * g.wgroup;
+  const int64_t n2 = 8 * (((int64_t)a.batch * a.n_head + 7) / 8) * ((a.t_q + kAQ - 1) / kAQ);
+  if (n1 > INT32_MAX || n2 > INT32_MAX) return hipErrorInvalidConfiguration;
   if (d_rope == 64) {
-    hipLaunchKernelGGL(prefill_decompress<64>, g1, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(prefill_attend<64>, g2, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(prefill_decompress<64>, dim3((unsigned)n1), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL(prefill_attend<64>, dim3((unsigned)n2), dim3(256), 0, stream, g);
   } else {
-    hipLaunchKernelGGL(prefill_decompress<0>, g1, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(prefill_attend<0>, g2, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(prefill_decompress<0>, dim3((unsigned)n1), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL(prefill_attend<0>, dim3((unsigned)n2), dim3(256), 0, stream, g);
   }
   return hipGetLastError();
 }
