@@ -437,3 +437,38 @@ def random_slots(key: int, num_slots: int, n_tok: int, n_skip: int = 0, n_out: i
 def random_positions(key: int, n_tok: int, max_pos: int) -> np.ndarray:
     """int32 positions uniform in [0, max_pos]."""
     return np.floor(uniforms(key, 0, n_tok) * (max_pos + 1)).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Context-parallel shares
+# --------------------------------------------------------------------------
+def dcp_local(case: Case, world: int, rank: int, interleave: int = 1, seed: int = 7,
+              spare_blocks: int = 2) -> tuple:
+    """The paged cache rank `rank` of `world` holds when the rows of every
+    request are dealt in runs of `interleave`: row j goes to rank
+    (j // interleave) % world.  The rank keeps its rows in order as a request
+    of its own in a fresh block pool (shuffled ids, NaN-poisoned spare blocks
+    and tails).  Returns (kv_local, block_table_local, local_lens).  Data
+    movement only: the stored values are copied unchanged."""
+    s = case.spec
+    lens = np.maximum(case.seq_lens.astype(np.int64), 0)
+    rows_of = []
+    for b in range(s.batch):
+        j = np.arange(int(lens[b]))
+        rows_of.append(j[(j // interleave) % world == rank])
+    n_loc = np.array([len(r) for r in rows_of], dtype=np.int64)
+    nblk = (n_loc + BLOCK_SIZE - 1) // BLOCK_SIZE
+    max_blocks = int(max(1, nblk.max(initial=0)))
+    num_blocks = int(nblk.sum()) + spare_blocks
+    perm = block_permutation(tensor_key(seed + 131 * rank + 7919 * world, "dcp_perm"), num_blocks)
+    table = np.full((s.batch, max_blocks), -1, dtype=np.int32)
+    kv = np.empty((num_blocks, BLOCK_SIZE, s.D), dtype=case.kv.dtype)
+    kv[...] = _poison(s.dtype)
+    used = 0
+    for b in range(s.batch):
+        table[b, :nblk[b]] = perm[used:used + nblk[b]]
+        used += int(nblk[b])
+        for lj, gj in enumerate(rows_of[b]):
+            gid = case.block_table[b, gj // BLOCK_SIZE]
+            kv[table[b, lj // BLOCK_SIZE], lj % BLOCK_SIZE] = case.kv[gid, gj % BLOCK_SIZE]
+    return kv, table, n_loc.astype(np.int32)

@@ -43,6 +43,9 @@ def _load():
     lib.mla_oracle_decode.restype = i64
     lib.mla_oracle_decode.argtypes = [i32, i32, i32, i32, i32, i32, vp, i32, vp, i32, i64, i32,
                                       vp, i32, vp, dbl, vp, i64, vp, vp]
+    lib.mla_oracle_decode_share.restype = i64
+    lib.mla_oracle_decode_share.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, i32, vp, i32, i64,
+                                            i32, vp, i32, vp, dbl, vp, i64, vp, vp]
     lib.mla_oracle_attend_absorbed.restype = i64
     lib.mla_oracle_attend_absorbed.argtypes = [i32, i32, i32, i32, i32, i32, i32, vp, vp, i32,
                                                vp, vp, i32, vp, i32, i64, i32, vp, i32, vp, dbl,
@@ -177,6 +180,63 @@ def decode(dims: Dims, t_q: int, q_abs, cache: Paged, scale_: float, sel=None,
                                     _p(bt), cache.max_blocks, _p(sl), float(scale_), _p(s), n_sel,
                                     _p(o), _p(lse))
     return o, lse, int(bad)
+
+
+def decode_share(dims: Dims, t_q: int, q_abs, cache: Paged, scale_: float, world: int, rank: int,
+                 interleave: int = 1, sel=None):
+    """One rank's share of decode context parallelism (two-pass attention over
+    the visible rows j with (j // interleave) % world == rank of the request's
+    whole paged cache).  Returns (o_lat [n][kv_rank], lse [n], n_invalid)."""
+    if not (world >= 1 and 0 <= rank < world and interleave >= 1):
+        raise ValueError("need world >= 1, 0 <= rank < world, interleave >= 1")
+    q_abs = _c(q_abs)
+    kv = _c(cache.kv)
+    bt = _c(cache.block_table.astype(np.int32, copy=False))
+    sl = _c(cache.seq_lens.astype(np.int32, copy=False))
+    s, n_sel = _sel(sel)
+    n = n_sel if s is not None else cache.batch * t_q * dims.n_head
+    o = np.empty((n, dims.kv_rank), np.float64)
+    lse = np.empty(n, np.float64)
+    bad = _load().mla_oracle_decode_share(int(world), int(rank), int(interleave), dims.n_head, dims.kv_rank,
+                                          dims.d_rope, cache.batch, t_q, _p(q_abs), _code(q_abs), _p(kv),
+                                          _code(kv), cache.num_blocks, cache.block_size, _p(bt),
+                                          cache.max_blocks, _p(sl), float(scale_), _p(s), n_sel, _p(o),
+                                          _p(lse))
+    return o, lse, int(bad)
+
+
+def lse_combine(o_parts, lse_parts):
+    """Combine partial attention results over disjoint row sets (the split
+    merge): with M = max_p lse_p and w_p = exp(lse_p - M),
+    o = sum_p w_p o_p / sum_p w_p and lse = M + ln sum_p w_p; parts with
+    lse = -inf carry no weight (their o is not read); all -inf gives zeros and
+    -inf; a NaN LSE in any part gives NaN.  o_parts [P][n][R], lse_parts
+    [P][n]; float64 results ([n][R], [n])."""
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    P, n = lse_parts.shape
+    o = np.zeros((n, o_parts.shape[2]), np.float64)
+    lse = np.full(n, -np.inf)
+    for k in range(n):
+        ls = lse_parts[:, k]
+        if np.isnan(ls).any():
+            o[k] = np.nan
+            lse[k] = np.nan
+            continue
+        M = ls.max()
+        if M == -np.inf:
+            continue
+        acc = np.zeros(o_parts.shape[2], np.float64)
+        wsum = 0.0
+        for p in range(P):
+            if ls[p] == -np.inf:
+                continue
+            wp = np.exp(ls[p] - M)
+            acc += wp * o_parts[p, k]
+            wsum += wp
+        o[k] = acc / wsum
+        lse[k] = M + np.log(wsum)
+    return o, lse
 
 
 def _full_args(dims, t_q, q_nope, q_pe, w_uk, w_uv, cache):

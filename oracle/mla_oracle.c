@@ -26,6 +26,8 @@
  *              CPUMLABackend, CPUMLAImpl.forward_mqa, do_kv_cache_update.
  *   [prolog]   Huawei CANN operator page "aclnnMlaProlog": the RmsNorm formula
  *              and the c^KV / k^R cache formulas.
+ *   [vllm cpu] also CPUMLAImpl construction: the context-parallel settings
+ *              dcp_world_size and cp_kv_cache_interleave_size.
  *
  * Pins (what each function is checked against, outside itself) are listed in
  * the test file that exercises it; every function below is pinned.
@@ -332,6 +334,82 @@ int64_t mla_oracle_decode(int method, int H, int kv_rank, int d_rope, int batch,
                               o_lat + k * kv_rank, lse + k);
       else
         bad += attend_online(&c, q_abs, q_dt, q_off, b, i, scale, o_lat + k * kv_rank, lse + k);
+    }
+    free(s_buf);
+  }
+  return bad;
+}
+
+/* One rank's share of decode context parallelism ([vllm cpu] CPUMLAImpl
+ * construction: dcp_world_size and cp_kv_cache_interleave_size).  The cache
+ * rows of a request are dealt to `world` ranks in runs of `interleave` rows:
+ * row j lives on rank (j / interleave) % world.  Rank `rank`'s share of one
+ * query is the two-pass attention of mla_oracle_decode restricted to the
+ * visible rows it holds:
+ *   o_r = sum over its rows of exp(s_j - m_r) row_j / Z_r,  lse_r = m_r + ln Z_r,
+ * with zeros and -inf when it holds none of them.  Combining the shares of all
+ * ranks with the split merge gives the full decode.  Reads the request's
+ * whole (global) paged cache; validity is the request's, as in decode.
+ * Returns the number of invalid items (outputs NaN). */
+static int attend_share(const paged* c, const void* q, int q_dt, int64_t q_off, int b, int i,
+                        double scale, int world, int rank, int interleave, double* s_buf,
+                        double* o_lat, double* lse) {
+  if (!request_valid(c, b)) {
+    fill(o_lat, c->kv_rank, NAN);
+    *lse = NAN;
+    return 1;
+  }
+  fill(o_lat, c->kv_rank, 0.0);
+  *lse = -INFINITY;
+  const int64_t L = c->seq_lens[b];
+  if (L == 0) return 0;
+  const int64_t n = horizon(L, c->t_q, i);
+  double m = -INFINITY;
+  int64_t held = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    if ((j / interleave) % world != rank) continue;
+    s_buf[j] = score(c, q, q_dt, q_off, row_base(c, b, j), scale);
+    if (s_buf[j] > m) m = s_buf[j];
+    ++held;
+  }
+  if (held == 0) return 0;
+  double Z = 0.0;
+  for (int64_t j = 0; j < n; ++j) {
+    if ((j / interleave) % world != rank) continue;
+    s_buf[j] = exp(s_buf[j] - m);
+    Z += s_buf[j];
+  }
+  for (int64_t j = 0; j < n; ++j) {
+    if ((j / interleave) % world != rank) continue;
+    const double p = s_buf[j] / Z;
+    const int64_t rb = row_base(c, b, j);
+    for (int l = 0; l < c->kv_rank; ++l) o_lat[l] += p * ld(c->kv, c->kv_dt, rb + l);
+  }
+  *lse = m + log(Z);
+  return 0;
+}
+
+int64_t mla_oracle_decode_share(int world, int rank, int interleave, int H, int kv_rank, int d_rope,
+                                int batch, int t_q, const void* q_abs, int q_dt, const void* kv,
+                                int kv_dt, int64_t num_blocks, int block_size,
+                                const int32_t* block_table, int max_blocks, const int32_t* seq_lens,
+                                double scale, const int32_t* sel, int64_t n_sel, double* o_lat,
+                                double* lse) {
+  paged c = make_paged(H, kv_rank, d_rope, batch, t_q, kv, kv_dt, num_blocks, block_size,
+                       block_table, max_blocks, seq_lens);
+  const int64_t n_items = sel ? n_sel : (int64_t)batch * t_q * H;
+  const int64_t Lmax = max_len(&c);
+  int64_t bad = 0;
+#pragma omp parallel reduction(+ : bad)
+  {
+    double* s_buf = (double*)malloc(sizeof(double) * (size_t)(Lmax > 0 ? Lmax : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t k = 0; k < n_items; ++k) {
+      int b, i, h;
+      item(sel, k, &c, &b, &i, &h);
+      const int64_t q_off = (((int64_t)b * t_q + i) * H + h) * c.D;
+      bad += attend_share(&c, q_abs, q_dt, q_off, b, i, scale, world, rank, interleave, s_buf,
+                          o_lat + k * kv_rank, lse + k);
     }
     free(s_buf);
   }
