@@ -157,6 +157,56 @@ mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch
                                 float* lse, void* workspace, size_t workspace_bytes,
                                 int32_t num_splits, void* stream);
 
+/* One rank's share of decode context parallelism (the vLLM CPU MLA backend
+ * page, CPUMLAImpl construction, names the settings dcp_world_size and
+ * cp_kv_cache_interleave_size; the pages print no distributed kernel, so the
+ * layout is the plain reading of those two settings).
+ *
+ * The rows of every request are dealt to dcp_world ranks in runs of
+ * dcp_interleave rows: global row j lives on rank (j / dcp_interleave) %
+ * dcp_world.  This call runs on rank dcp_rank: kv_cache and block_table hold
+ * ONLY that rank's rows, in increasing global order, as the rank's own paged
+ * request (its local row k is kv_cache[block_table[b][k / 16]][k % 16]).
+ * seq_lens are the GLOBAL lengths (all ranks' rows, queries included); query i
+ * sees the rows this rank holds among global rows 0 .. L - t_q + i.  Outputs
+ * are this rank's partial result over those rows: out_lat (normalised over
+ * them) and lse, both as in mla_decode_attention; a rank that holds none of a
+ * query's rows gives zeros and -inf.  Combining the shares of all ranks with
+ * mla_lse_combine gives mla_decode_attention's result.  Float32 out_lat keeps
+ * the combine exact to float32; bf16 is accepted.
+ *
+ * Arguments and errors as mla_decode_attention (max_blocks and the workspace
+ * size refer to the rank's own table), plus MLA_ERR_ARG for dcp_world < 1,
+ * dcp_rank outside [0, dcp_world) or dcp_interleave < 1, and MLA_ERR_NULL for
+ * a NULL lse (required: a share without its LSE cannot be combined).  The data
+ * errors are judged on the rank's view: a length beyond the rank's table is
+ * MLA_DATA_LEN_OVER_TABLE.  dcp_world == 1 is mla_decode_attention. */
+mla_status mla_decode_attention_dcp(const mla_dims* dims, float scale, int32_t batch, int32_t t_q,
+                                    const void* q_abs, const void* kv_cache, mla_dtype dt,
+                                    int64_t num_blocks, int32_t block_size,
+                                    const int32_t* block_table, int32_t max_blocks,
+                                    const int32_t* seq_lens, int32_t dcp_world, int32_t dcp_rank,
+                                    int32_t dcp_interleave, void* out_lat, mla_dtype out_dt,
+                                    float* lse, void* workspace, size_t workspace_bytes,
+                                    int32_t num_splits, void* stream);
+
+/* LSE combine of n_parts partial attention results over disjoint row sets
+ * (the split merge of step 2, here across context-parallel ranks after the
+ * all-gather of their shares):
+ *   M = max_p lse[p][r],  w_p = exp(lse[p][r] - M),
+ *   out[r] = sum_p w_p o[p][r] / sum_p w_p,  lse_out[r] = M + ln sum_p w_p.
+ * Parts with lse = -inf carry no weight (their vectors are not read); all
+ * parts -inf gives zeros and -inf; a NaN lse in any part gives NaN.
+ * o_parts float32 [n_parts][n_rows][width], lse_parts float32
+ * [n_parts][n_rows], out [n_rows][width] type out_dt, lse_out float32
+ * [n_rows] or NULL.  Float32 arithmetic, parts added in index order
+ * (deterministic).  Asynchronous on `stream`.
+ * Errors: MLA_ERR_SHAPE (width < 1, n_rows < 0, n_parts < 1), MLA_ERR_ARG
+ * (bad dtype code), MLA_ERR_NULL, MLA_ERR_HIP. */
+mla_status mla_lse_combine(int32_t width, int64_t n_rows, int32_t n_parts, const float* o_parts,
+                           const float* lse_parts, void* out, mla_dtype out_dt, float* lse_out,
+                           void* stream);
+
 /* Step 3: decompress the latent output once through W_UV (memra mla.rs,
  * mla_attend_absorbed, decompress step):
  *   out[n][h][j] = sum_l w_uv[h][j][l] * o_lat[n][h][l]

@@ -6,8 +6,10 @@ attention over the paged latent cache plus the LSE-weighted merge) and
 ``mla_decompress_v`` (one W_UV decompression).  Upstream of attention,
 ``mla_cache_append`` writes the new tokens' RmsNorm'd and rope'd latent rows
 into the paged cache and rotates the query rope part; ``mla_prefill_attention``
-runs the naive (multi-head) form for prefill and chunked prefill.  See
-include/mla.h for the contract of every entry point.
+runs the naive (multi-head) form for prefill and chunked prefill;
+``mla_decode_attention_dcp`` runs one rank's share of context-parallel decode
+and ``mla_lse_combine`` merges the ranks' shares.  See include/mla.h for the
+contract of every entry point.
 """
 from ._binding import (  # noqa: F401
     EXPORTS,
@@ -27,12 +29,14 @@ from ._binding import (  # noqa: F401
     mla_absorb_q,
     mla_cache_append,
     mla_decode_attention,
+    mla_decode_attention_dcp,
     mla_decode_resolve_splits,
     mla_decode_status,
     mla_decode_workspace_size,
     mla_decompress_v,
     mla_default_scale,
     mla_dims,
+    mla_lse_combine,
     mla_prefill_attention,
     mla_prefill_workspace_size,
     mla_status_string,

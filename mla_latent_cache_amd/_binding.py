@@ -25,7 +25,7 @@ MLA_ROPE_NEOX, MLA_ROPE_INTERLEAVED = 0, 1
 EXPORTS = ("mla_default_scale", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode_resolve_splits", "mla_decode_attention", "mla_decompress_v",
            "mla_decode_status", "mla_status_string", "mla_cache_append", "mla_prefill_workspace_size",
-           "mla_prefill_attention")
+           "mla_prefill_attention", "mla_decode_attention_dcp", "mla_lse_combine")
 
 
 class MlaError(RuntimeError):
@@ -66,6 +66,11 @@ def lib():
     L.mla_decode_attention.restype = ctypes.c_int
     L.mla_decode_attention.argtypes = [P, f32, i32, i32, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
                                        vp, ctypes.c_int, vp, vp, sz, i32, vp]
+    L.mla_decode_attention_dcp.restype = ctypes.c_int
+    L.mla_decode_attention_dcp.argtypes = [P, f32, i32, i32, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
+                                           i32, i32, i32, vp, ctypes.c_int, vp, vp, sz, i32, vp]
+    L.mla_lse_combine.restype = ctypes.c_int
+    L.mla_lse_combine.argtypes = [i32, i64, i32, vp, vp, vp, ctypes.c_int, vp, vp]
     L.mla_decompress_v.restype = ctypes.c_int
     L.mla_decompress_v.argtypes = [P, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp]
     L.mla_decode_status.restype = ctypes.c_int
@@ -177,6 +182,33 @@ def mla_decode_attention(dims: DimsLike, scale: float, q_abs, kv_cache, block_ta
         int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]),
         _ptr(seq_lens), _ptr(out_lat), _dt(out_lat), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), int(num_splits), _stream(stream)))
+
+
+def mla_decode_attention_dcp(dims: DimsLike, scale: float, q_abs, kv_cache, block_table, seq_lens, dcp_world: int,
+                             dcp_rank: int, dcp_interleave: int, out_lat, lse, workspace, num_splits: int = 0,
+                             stream=None) -> None:
+    """One rank's share of decode context parallelism: kv_cache / block_table
+    hold the rank's rows only, seq_lens are the global lengths; out_lat and
+    lse (required) receive the rank's partial result."""
+    d = as_dims(dims)
+    B, t_q = int(q_abs.shape[0]), int(q_abs.shape[1])
+    if workspace is None:
+        raise ValueError("mla_decode_attention_dcp needs a workspace tensor")
+    _check("mla_decode_attention_dcp", lib().mla_decode_attention_dcp(
+        ctypes.byref(d), float(scale), B, t_q, _ptr(q_abs), _ptr(kv_cache), _dt(kv_cache),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]),
+        _ptr(seq_lens), int(dcp_world), int(dcp_rank), int(dcp_interleave), _ptr(out_lat), _dt(out_lat), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), int(num_splits), _stream(stream)))
+
+
+def mla_lse_combine(o_parts, lse_parts, out, lse_out=None, stream=None) -> None:
+    """Combine partial results: o_parts float32 [P][n][width], lse_parts
+    float32 [P][n], out [n][width] (f32 or bf16), lse_out float32 [n] or None."""
+    P = int(lse_parts.shape[0])
+    n = lse_parts.numel() // max(1, P)
+    width = o_parts.numel() // max(1, P * n)
+    _check("mla_lse_combine", lib().mla_lse_combine(int(width), int(n), P, _ptr(o_parts), _ptr(lse_parts), _ptr(out),
+                                                    _dt(out), _ptr(lse_out), _stream(stream)))
 
 
 def mla_decompress_v(dims: DimsLike, o_lat, w_uv, out, stream=None) -> None:

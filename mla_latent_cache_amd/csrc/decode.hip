@@ -42,10 +42,23 @@ namespace {
 
 constexpr uint32_t kNegLen = 0x1u, kLenOverTable = 0x2u, kLenBelowTq = 0x4u, kBadBlock = 0x8u;
 
-__device__ __forceinline__ uint32_t request_flags(int64_t L, int t_q, int max_blocks) {
-  if (L < 0) return kNegLen;
+// Rows j < x that this rank holds when the rows of a request are dealt to
+// `world` ranks in runs of `il` (row j on rank (j / il) % world, the context-
+// parallel layout whose settings the vLLM CPU MLA backend page names); x
+// itself on a single rank.  A rank keeps its rows in order, so the rows below
+// any global position form a prefix of its own rows.
+__device__ __forceinline__ int64_t held_rows(int64_t x, int world, int rank, int il) {
+  if (world == 1) return x;
+  if (x <= 0) return 0;
+  const int64_t full = x / il, rem = x - full * il;
+  return ((full + world - 1 - rank) / world) * il + (full % world == rank ? rem : 0);
+}
+
+// Data errors of a request of global length Lg holding L rows here.
+__device__ __forceinline__ uint32_t request_flags(int64_t Lg, int64_t L, int t_q, int max_blocks) {
+  if (Lg < 0) return kNegLen;
   if (L > (int64_t)max_blocks * 16) return kLenOverTable;
-  if (L > 0 && L < t_q) return kLenBelowTq;
+  if (Lg > 0 && Lg < t_q) return kLenBelowTq;
   return 0u;
 }
 
@@ -164,8 +177,11 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   auto wave_of = [](int h, int d) { return h + 2 * ((d + 2) & 3); };  // wave holding (qh, dq)
   const int l16 = lane & 15, g = lane >> 4;
 
-  const int64_t L = a.seq_lens[b];
-  uint32_t flags = request_flags(L, a.t_q, a.max_blocks);
+  // Lengths count global rows; L and the query horizons count the rows this
+  // rank holds (all of them on a single rank).
+  const int64_t Lg = a.seq_lens[b];
+  const int64_t L = held_rows(Lg, a.dcp_world, a.dcp_rank, a.dcp_interleave);
+  uint32_t flags = request_flags(Lg, L, a.t_q, a.max_blocks);
   const int64_t r_begin = (int64_t)s * a.chunk_blocks * 16;
   int64_t r_end = r_begin + (int64_t)a.chunk_blocks * 16;
   if (flags || r_end > L) r_end = flags ? r_begin : L;
@@ -190,7 +206,8 @@ __global__ __launch_bounds__(512, 1) void decode_split_mfma(const DecodeArgs a) 
   {
     const int qr = mt * kQRowsPerWG + fq;
     const bool ok = qr < a.n_q;
-    const int64_t horizon = L - a.t_q + (ok ? qr / a.n_head : 0) + 1;
+    const int64_t horizon =
+        held_rows(Lg - a.t_q + (ok ? qr / a.n_head : 0) + 1, a.dcp_world, a.dcp_rank, a.dcp_interleave);
     const int64_t vis_end = horizon < r_end ? horizon : r_end;
     vis_lim = !ok || vis_end <= r_begin ? 0 : (int)(vis_end - r_begin);
   }
@@ -578,12 +595,13 @@ __global__ __launch_bounds__(128) void decode_split_generic(const DecodeArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int D = a.kv_rank + a.d_rope, R = a.kv_rank;
 
-  const int64_t L = a.seq_lens[b];
-  uint32_t flags = request_flags(L, a.t_q, a.max_blocks);
+  const int64_t Lg = a.seq_lens[b];
+  const int64_t L = held_rows(Lg, a.dcp_world, a.dcp_rank, a.dcp_interleave);
+  uint32_t flags = request_flags(Lg, L, a.t_q, a.max_blocks);
   const int64_t r_begin = (int64_t)s * a.chunk_blocks * 16;
   int64_t r_end = r_begin + (int64_t)a.chunk_blocks * 16;
   if (flags || r_end > L) r_end = flags ? r_begin : L;
-  const int64_t horizon = L - a.t_q + q / a.n_head + 1;
+  const int64_t horizon = held_rows(Lg - a.t_q + q / a.n_head + 1, a.dcp_world, a.dcp_rank, a.dcp_interleave);
   if (r_end > horizon) r_end = horizon > r_begin ? horizon : r_begin;
 
   const TS* qp = static_cast<const TS*>(a.q) + ((int64_t)b * a.n_q + q) * D;
@@ -911,7 +929,61 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_merge_wide(const Decod
   if (tid == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
 }
 
+// LSE combine of P partial results over disjoint row sets (the split merge,
+// here across context-parallel ranks): one wave per row.  With M the largest
+// part LSE and w_p = exp(lse_p - M), o = sum_p w_p o_p / sum_p w_p and
+// lse = M + ln sum_p w_p; parts with lse -inf carry no weight and their
+// vectors are not read; all -inf gives zeros and -inf; a NaN LSE in any part
+// gives NaN.  Deterministic: parts are added in index order.
+constexpr int kCombineRows = 4;  // rows (waves) per workgroup
+__global__ __launch_bounds__(64 * kCombineRows) void lse_combine_kernel(int64_t n_rows, int n_parts, int width,
+                                                                        const float* __restrict__ o_parts,
+                                                                        const float* __restrict__ lse_parts,
+                                                                        void* out, int out_bf16, float* lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  float M = -INFINITY;
+  bool nan_seen = false;
+  for (int p = lane; p < n_parts; p += 64) {
+    const float v = lse_parts[(int64_t)p * n_rows + row];
+    nan_seen |= isnan(v);
+    M = fmaxf(M, v);
+  }
+  M = wave_max(M);
+  const bool any_nan = __ballot(nan_seen) != 0;
+  float wsum = 0.f;
+  for (int p = lane; p < n_parts; p += 64) {
+    const float v = lse_parts[(int64_t)p * n_rows + row];
+    wsum += (v == -INFINITY || M == -INFINITY) ? 0.f : __expf(v - M);
+  }
+  wsum = wave_sum(wsum);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  for (int c = lane; c < width; c += 64) {
+    float acc = 0.f;
+    for (int p = 0; p < n_parts; ++p) {
+      const float v = lse_parts[(int64_t)p * n_rows + row];  // uniform across the wave
+      if (v == -INFINITY || M == -INFINITY) continue;
+      acc += __expf(v - M) * o_parts[((int64_t)p * n_rows + row) * width + c];
+    }
+    const float r = any_nan ? NAN : acc * inv;
+    if (out_bf16) static_cast<uint16_t*>(out)[row * width + c] = f32_to_bf16(r);
+    else static_cast<float*>(out)[row * width + c] = r;
+  }
+  if (lane == 0 && lse_out) lse_out[row] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
+}
+
 }  // namespace
+
+hipError_t launch_lse_combine(int64_t n_rows, int n_parts, int width, const float* o_parts, const float* lse_parts,
+                              void* out, bool out_bf16, float* lse_out, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  const int64_t grid = (n_rows + kCombineRows - 1) / kCombineRows;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)grid), dim3(64 * kCombineRows), 0, stream, n_rows, n_parts,
+                     width, o_parts, lse_parts, out, (int)out_bf16, lse_out);
+  return hipGetLastError();
+}
 
 Plan decode_plan(int n_head, int kv_rank, int d_rope, int batch, int t_q, int max_blocks,
                  int splits, bool bf16) {

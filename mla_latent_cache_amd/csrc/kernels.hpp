@@ -40,6 +40,7 @@ struct DecodeArgs {
   float scale;             // softmax scale
   int out_bf16;            // out dtype is bfloat16
   int direct;              // splits == 1: write final outputs, no merge
+  int dcp_world, dcp_rank, dcp_interleave;  // context-parallel share (1, 0, 1: all rows)
 };
 
 struct Plan {
@@ -53,6 +54,9 @@ Plan decode_plan(int n_head, int kv_rank, int d_rope, int batch, int t_q, int ma
                  int splits, bool bf16);
 
 hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t stream);
+
+hipError_t launch_lse_combine(int64_t n_rows, int n_parts, int width, const float* o_parts, const float* lse_parts,
+                              void* out, bool out_bf16, float* lse_out, hipStream_t stream);
 
 hipError_t launch_absorb(int n_head, int d_nope, int d_rope, int kv_rank, int64_t n_tok,
                          const void* q_nope, const void* q_pe, const void* w_uk, bool in_bf16,

@@ -141,11 +141,12 @@ mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_
   return MLA_OK;
 }
 
-mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_abs,
-                                const void* kv_cache, mla_dtype dt, int64_t num_blocks, int32_t block_size,
-                                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
-                                void* out_lat, mla_dtype out_dt, float* lse, void* workspace,
-                                size_t workspace_bytes, int32_t num_splits, void* stream) {
+static mla_status decode_impl(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_abs,
+                              const void* kv_cache, mla_dtype dt, int64_t num_blocks, int32_t block_size,
+                              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                              int32_t dcp_world, int32_t dcp_rank, int32_t dcp_interleave, void* out_lat,
+                              mla_dtype out_dt, float* lse, void* workspace, size_t workspace_bytes,
+                              int32_t num_splits, void* stream) {
   const mla_status st = check_decode_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 0 || t_q < 1 || max_blocks < 1 || num_blocks < 1 || num_splits < 0) return MLA_ERR_SHAPE;
@@ -197,7 +198,43 @@ mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch
   a.scale = scale;
   a.out_bf16 = out_dt == MLA_BF16;
   a.direct = p.splits == 1;
+  a.dcp_world = dcp_world;
+  a.dcp_rank = dcp_rank;
+  a.dcp_interleave = dcp_interleave;
   const hipError_t e = mla::launch_decode(a, mfma, bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_abs,
+                                const void* kv_cache, mla_dtype dt, int64_t num_blocks, int32_t block_size,
+                                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                void* out_lat, mla_dtype out_dt, float* lse, void* workspace,
+                                size_t workspace_bytes, int32_t num_splits, void* stream) {
+  return decode_impl(dims, scale, batch, t_q, q_abs, kv_cache, dt, num_blocks, block_size, block_table, max_blocks,
+                     seq_lens, 1, 0, 1, out_lat, out_dt, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+mla_status mla_decode_attention_dcp(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_abs,
+                                    const void* kv_cache, mla_dtype dt, int64_t num_blocks, int32_t block_size,
+                                    const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                    int32_t dcp_world, int32_t dcp_rank, int32_t dcp_interleave, void* out_lat,
+                                    mla_dtype out_dt, float* lse, void* workspace, size_t workspace_bytes,
+                                    int32_t num_splits, void* stream) {
+  if (dcp_world < 1 || dcp_rank < 0 || dcp_rank >= dcp_world || dcp_interleave < 1) return MLA_ERR_ARG;
+  if (!lse && batch > 0) return MLA_ERR_NULL;  // a share is only usable with its LSE
+  return decode_impl(dims, scale, batch, t_q, q_abs, kv_cache, dt, num_blocks, block_size, block_table, max_blocks,
+                     seq_lens, dcp_world, dcp_rank, dcp_interleave, out_lat, out_dt, lse, workspace,
+                     workspace_bytes, num_splits, stream);
+}
+
+mla_status mla_lse_combine(int32_t width, int64_t n_rows, int32_t n_parts, const float* o_parts,
+                           const float* lse_parts, void* out, mla_dtype out_dt, float* lse, void* stream) {
+  if (width < 1 || n_rows < 0 || n_parts < 1) return MLA_ERR_SHAPE;
+  if (!dt_ok(out_dt)) return MLA_ERR_ARG;
+  if (n_rows == 0) return MLA_OK;
+  if (!o_parts || !lse_parts || !out) return MLA_ERR_NULL;
+  const hipError_t e = mla::launch_lse_combine(n_rows, n_parts, width, o_parts, lse_parts, out, out_dt == MLA_BF16,
+                                               lse, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -210,3 +210,31 @@ def test_binding_rejects_host_tensors():
         mla.mla_absorb_q(GLM52, x, torch.zeros(4, 64, 64, dtype=torch.bfloat16),
                          torch.zeros(64, 192, 512, dtype=torch.bfloat16),
                          torch.zeros(4, 64, 576, dtype=torch.bfloat16))
+
+
+def test_dcp_and_combine_host_validation():
+    # Argument errors are reported before any device work (no GPU needed).
+    L = mla.lib()
+    fake = ctypes.c_void_p(0x1000)
+    dims = mla.as_dims(GLM52)
+
+    def dcp(world=2, rank=0, interleave=1, lse=fake, batch=2):
+        return L.mla_decode_attention_dcp(ctypes.byref(dims), 0.0625, batch, 1, fake, fake, B.MLA_BF16, 64, 16,
+                                          fake, 8, fake, world, rank, interleave, fake, B.MLA_F32, lse, fake,
+                                          1 << 20, 0, None)
+    assert dcp(world=0) == B.MLA_ERR_ARG
+    assert dcp(rank=-1) == B.MLA_ERR_ARG
+    assert dcp(rank=2) == B.MLA_ERR_ARG
+    assert dcp(interleave=0) == B.MLA_ERR_ARG
+    assert dcp(lse=None) == B.MLA_ERR_NULL
+
+    def comb(width=512, n_rows=4, n_parts=2, o=fake, l=fake, out=fake, dt=B.MLA_F32):
+        return L.mla_lse_combine(width, n_rows, n_parts, o, l, out, dt, None, None)
+    assert comb(width=0) == B.MLA_ERR_SHAPE
+    assert comb(n_rows=-1) == B.MLA_ERR_SHAPE
+    assert comb(n_parts=0) == B.MLA_ERR_SHAPE
+    assert comb(dt=5) == B.MLA_ERR_ARG
+    assert comb(o=None) == B.MLA_ERR_NULL
+    assert comb(l=None) == B.MLA_ERR_NULL
+    assert comb(out=None) == B.MLA_ERR_NULL
+    assert comb(n_rows=0, o=None, l=None, out=None) == B.MLA_OK
