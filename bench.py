@@ -206,6 +206,80 @@ def time_prolog(spec, case, dims, kv, stream, reps: int = 20, chunk: int = 4096)
     }
 
 
+def time_dcp(spec, case, dims, q_abs, stream, world: int = 8, interleave: int = 1, reps: int = 20):
+    """One GPU's part of context-parallel decode at `world` ranks, timed with
+    HIP events: rank 0's share of the workload (its rows only, float32 partial
+    and LSE), and the combine of `world` shares into the final bf16 result.
+    The all-gather between the two runs over the GPU links and is not part of
+    one GPU's work."""
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_latent_cache_amd as mla
+
+    B, T, H, D, R = spec.batch, spec.t_q, spec.n_head, spec.D, spec.kv_rank
+    e = 2 if spec.dtype == "bf16" else 4
+    kv, bt, n_loc = mi.dcp_local(case, world, 0, interleave)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    kv_d, bt_d, sl_d = dev(kv), dev(bt), dev(case.seq_lens)
+    o = torch.empty(B, T, H, R, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.mla_decode_workspace_size(dims, B, T, bt.shape[1], 16, 0), dtype=torch.uint8, device="cuda")
+    n = B * T * H
+    o_parts = torch.empty(world, n, R, dtype=torch.float32, device="cuda")
+    l_parts = torch.empty(world, n, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, R, dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.empty(n, dtype=torch.float32, device="cuda")
+
+    def share():
+        mla.mla_decode_attention_dcp(dims, case.scale, q_abs, kv_d, bt_d, sl_d, world, 0, interleave, o, lse, ws,
+                                     0, stream)
+
+    def combine():
+        mla.mla_lse_combine(o_parts, l_parts, out, lse_out, stream)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in es:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in es) / reps * 1e-3
+
+    t_share = timed(share)
+    if mla.mla_decode_status(ws, stream) != 0:
+        raise RuntimeError("context-parallel benchmark: the share reported a data error")
+    for k in range(world):  # every part a valid share (the combine's time does not depend on values)
+        o_parts[k].copy_(o.reshape(n, R))
+        l_parts[k].copy_(lse.reshape(n))
+    t_comb = timed(combine)
+    rows = int(np.asarray(n_loc, dtype=np.int64).sum())
+    b_share = rows * D * e + n * D * e + n * R * 4 + n * 4 + int(((n_loc + 15) // 16).sum()) * 4 + B * 4
+    b_comb = world * n * (R + 1) * 4 + n * R * 2 + n * 4
+    return {
+        "layout": f"{world} ranks, rows dealt in runs of {interleave} (row j on rank (j / {interleave}) % {world})",
+        "share_rows": rows,
+        "share_us": round(t_share * 1e6, 2),
+        "share_bytes": b_share,
+        "share_gbs": round(b_share / t_share / 1e9, 1),
+        "share_frac": round(b_share / t_share / 1e9 / HBM_PEAK_GBS, 4),
+        "combine_parts": world,
+        "combine_us": round(t_comb * 1e6, 2),
+        "combine_bytes": b_comb,
+        "combine_gbs": round(b_comb / t_comb / 1e9, 1),
+        "combine_frac": round(b_comb / t_comb / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def prefill_figures(spec, seq_lens):
     """Algorithmic work of one naive-form prefill call: flops of the
     decompression GEMM (every cache row of a request through W_UK and W_UV)
@@ -294,6 +368,7 @@ def main() -> int:
     ap.add_argument("--cpu-items", type=int, default=4096, help="oracle items for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the naive-form prefill measurement")
+    ap.add_argument("--no-dcp", action="store_true", help="skip the context-parallel share measurement")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel of a timed step from the host instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -431,6 +506,8 @@ def main() -> int:
     prolog = time_prolog(spec, case, dims, copies[0]["kv"], stream)
     stage["cache_append"] = prolog["decode_step_us"] * 1e-3
     prefill = None if args.no_prefill else time_prefill()
+    dcp = time_dcp(spec, case, dims, copies[0]["q_abs"], stream) if (spec.name == "glm52_decode" and not args.no_dcp) \
+        else None
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -470,6 +547,7 @@ def main() -> int:
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "prolog": prolog,
         "prefill": prefill,
+        "dcp": dcp,
         "roofline": {
             "kernel": "decode call: decode_split_mfma + decode_merge",
             "bound": "hbm",

@@ -934,12 +934,17 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_merge_wide(const Decod
 // part LSE and w_p = exp(lse_p - M), o = sum_p w_p o_p / sum_p w_p and
 // lse = M + ln sum_p w_p; parts with lse -inf carry no weight and their
 // vectors are not read; all -inf gives zeros and -inf; a NaN LSE in any part
-// gives NaN.  Deterministic: parts are added in index order.
+// gives NaN.  Deterministic: parts are added in index order.  Lane l owns
+// columns 4 l .. + 3 of every 256-column chunk; the weights of 64 parts at a
+// time are formed once (lane p holds part p's) and broadcast, and the part
+// vectors go out eight at a time before they are summed, so the row costs a
+// few memory latencies rather than one per part.
 constexpr int kCombineRows = 4;  // rows (waves) per workgroup
 __global__ __launch_bounds__(64 * kCombineRows) void lse_combine_kernel(int64_t n_rows, int n_parts, int width,
                                                                         const float* __restrict__ o_parts,
                                                                         const float* __restrict__ lse_parts,
-                                                                        void* out, int out_bf16, float* lse_out) {
+                                                                        void* out, int out_bf16, float* lse_out,
+                                                                        int vec) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kCombineRows + (threadIdx.x >> 6);
   if (row >= n_rows) return;
@@ -952,23 +957,51 @@ __global__ __launch_bounds__(64 * kCombineRows) void lse_combine_kernel(int64_t 
   }
   M = wave_max(M);
   const bool any_nan = __ballot(nan_seen) != 0;
-  float wsum = 0.f;
-  for (int p = lane; p < n_parts; p += 64) {
+  auto weight = [&](int p) {  // weight of part p (0 past the last part or for an empty part)
+    if (p >= n_parts || M == -INFINITY) return 0.f;
     const float v = lse_parts[(int64_t)p * n_rows + row];
-    wsum += (v == -INFINITY || M == -INFINITY) ? 0.f : __expf(v - M);
-  }
+    return v == -INFINITY ? 0.f : __expf(v - M);
+  };
+  float wsum = 0.f;
+  for (int p = lane; p < n_parts; p += 64) wsum += weight(p);
   wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int c = lane; c < width; c += 64) {
-    float acc = 0.f;
-    for (int p = 0; p < n_parts; ++p) {
-      const float v = lse_parts[(int64_t)p * n_rows + row];  // uniform across the wave
-      if (v == -INFINITY || M == -INFINITY) continue;
-      acc += __expf(v - M) * o_parts[((int64_t)p * n_rows + row) * width + c];
+  const float* orow = o_parts + row * width;
+  const int64_t pstride = n_rows * width;
+  for (int c0 = 0; c0 < width; c0 += 256) {
+    const int c = c0 + 4 * lane;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < n_parts; p0 += 64) {
+      const float wl = weight(p0 + lane);  // lane k: weight of part p0 + k
+      const int np = n_parts - p0 < 64 ? n_parts - p0 : 64;
+      for (int k0 = 0; k0 < np; k0 += 8) {
+        f32x4 v[8];
+        float wk[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          wk[k] = __shfl(wl, k0 + k, 64);
+          v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (k0 + k < np && wk[k] != 0.f && c < width) {
+            const float* src = orow + (int64_t)(p0 + k0 + k) * pstride + c;
+            if (vec) {
+              v[k] = *reinterpret_cast<const f32x4*>(src);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[k][e] = c + e < width ? src[e] : 0.f;
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += wk[k] * v[k];
+      }
     }
-    const float r = any_nan ? NAN : acc * inv;
-    if (out_bf16) static_cast<uint16_t*>(out)[row * width + c] = f32_to_bf16(r);
-    else static_cast<float*>(out)[row * width + c] = r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (c + e >= width) break;
+      const float r = any_nan ? NAN : acc[e] * inv;
+      if (out_bf16) static_cast<uint16_t*>(out)[row * width + c + e] = f32_to_bf16(r);
+      else static_cast<float*>(out)[row * width + c + e] = r;
+    }
   }
   if (lane == 0 && lse_out) lse_out[row] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
 }
@@ -981,7 +1014,8 @@ hipError_t launch_lse_combine(int64_t n_rows, int n_parts, int width, const floa
   const int64_t grid = (n_rows + kCombineRows - 1) / kCombineRows;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(lse_combine_kernel, dim3((unsigned)grid), dim3(64 * kCombineRows), 0, stream, n_rows, n_parts,
-                     width, o_parts, lse_parts, out, (int)out_bf16, lse_out);
+                     width, o_parts, lse_parts, out, (int)out_bf16, lse_out,
+                     (int)((width & 3) == 0 && (reinterpret_cast<uintptr_t>(o_parts) & 15) == 0));
   return hipGetLastError();
 }
 
