@@ -472,3 +472,45 @@ def dcp_local(case: Case, world: int, rank: int, interleave: int = 1, seed: int 
             gid = case.block_table[b, gj // BLOCK_SIZE]
             kv[table[b, lj // BLOCK_SIZE], lj % BLOCK_SIZE] = case.kv[gid, gj % BLOCK_SIZE]
     return kv, table, n_loc.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Fused prolog inputs
+# --------------------------------------------------------------------------
+PROLOG_HIDDEN, PROLOG_Q_RANK = 6144, 1536  # the pages fix neither; see the design notes
+
+
+@dataclass
+class PrologInputs:
+    x: np.ndarray          # [n_tok][hidden]
+    w_dq: np.ndarray       # [q_rank][hidden]
+    w_uq: np.ndarray       # [H d_nope][q_rank]
+    w_qr: np.ndarray       # [H d_rope][q_rank]
+    w_dkv: np.ndarray      # [kv_rank][hidden]
+    w_kr: np.ndarray       # [d_rope][hidden]
+    gamma_q: np.ndarray    # [q_rank]
+    gamma_kv: np.ndarray   # [kv_rank]
+
+
+def prolog_inputs(spec: Spec, n_tok: int, hidden: int = PROLOG_HIDDEN, q_rank: int = PROLOG_Q_RANK,
+                  tag: str = "prolog") -> PrologInputs:
+    """Hidden states x ~ N(0, 1) (the output of the layer's input norm) and
+    projection weights ~ N(0, 1) / sqrt(fan-in), stored [out][in] in the
+    spec's dtype; norm gains 1 + 0.1 N(0, 1).  W_UK comes from the decode case
+    of the same spec."""
+    H, dn, dr, R = spec.n_head, spec.d_nope, spec.d_rope, spec.kv_rank
+
+    def draw(name, shape, scale):
+        n = int(np.prod(shape))
+        return store((normals(tensor_key(spec.seed, f"{tag}_{name}"), 0, n) * scale).reshape(shape), spec.dtype)
+
+    return PrologInputs(
+        x=draw("x", (n_tok, hidden), 1.0),
+        w_dq=draw("w_dq", (q_rank, hidden), 1.0 / math.sqrt(hidden)),
+        w_uq=draw("w_uq", (H * dn, q_rank), 1.0 / math.sqrt(q_rank)),
+        w_qr=draw("w_qr", (H * dr, q_rank), 1.0 / math.sqrt(q_rank)),
+        w_dkv=draw("w_dkv", (R, hidden), 1.0 / math.sqrt(hidden)),
+        w_kr=draw("w_kr", (dr, hidden), 1.0 / math.sqrt(hidden)),
+        gamma_q=store(1.0 + 0.1 * normals(tensor_key(spec.seed, f"{tag}_gq"), 0, q_rank), spec.dtype),
+        gamma_kv=store(1.0 + 0.1 * normals(tensor_key(spec.seed, f"{tag}_gkv"), 0, R), spec.dtype),
+    )

@@ -362,3 +362,42 @@ def cache_append(cache_rows, kv_rank: int, c_kv, k_pe, gamma, eps: float, positi
         0 if g is None else _code(g), float(eps), _p(pos), float(base), int(style), _p(sl),
         _p(cache_rows), num_slots)
     return int(bad)
+
+
+def prolog(dims: Dims, x, w_dq, w_uq, w_qr, w_uk, w_dkv, w_kr, gamma_q, gamma_kv, eps_q: float, eps_kv: float,
+           positions, base: float, style: int, slots, cache_rows):
+    """The fused MLA prolog (CANN aclnnMlaProlog, its four paths), in the
+    order the page's formulas give, float64 throughout:
+        c^Q  = RmsNorm(x W^DQ)             (gamma_q, eps_q)
+        q^C  = c^Q W^UQ,  q^N = q^C W^UK   (per head; W^UK is the absorb step's)
+        q^R  = ROPE(c^Q W^QR)              (each token at its position)
+        c^KV = RmsNorm(x W^DKV), k^R = ROPE(x W^KR), both written to cache
+               row slots[n] (the cache append: gamma_kv, eps_kv)
+    Weights are stored [out][in]: w_dq [q_rank][hidden], w_dkv
+    [kv_rank][hidden], w_kr [d_rope][hidden], w_uq [H d_nope][q_rank] and
+    w_qr [H d_rope][q_rank] (output feature h * width + j); w_uk
+    [H][d_nope][kv_rank].  x [n][hidden].  cache_rows float64
+    [num_slots][kv_rank + d_rope] is updated in place.  Returns
+    (q_abs [n][H][kv_rank + d_rope] = [q^N | q^R], out-of-range slot count).
+    """
+    H, dn, dr, R = dims.n_head, dims.d_nope, dims.d_rope, dims.kv_rank
+    x = np.asarray(_widen(x), np.float64)
+    n = x.shape[0]
+    cq = rmsnorm(x @ np.asarray(_widen(w_dq), np.float64).T, gamma_q, eps_q)
+    qc = (cq @ np.asarray(_widen(w_uq), np.float64).T).reshape(n, H, dn)
+    qr = np.zeros((n, H, 0), np.float64)
+    if dr:
+        qr = rope_rows((cq @ np.asarray(_widen(w_qr), np.float64).T).reshape(n, H, dr), positions, base, style)
+    q_abs = absorb(dims, qc, qr, w_uk).reshape(n, H, R + dr)
+    ckv = x @ np.asarray(_widen(w_dkv), np.float64).T
+    kr = x @ np.asarray(_widen(w_kr), np.float64).T if dr else None
+    bad = cache_append(cache_rows, R, ckv, kr, gamma_kv, eps_kv, positions, base, style, slots)
+    return q_abs, bad
+
+
+def _widen(a):
+    """Stored values as float64 (bfloat16 bit patterns widened exactly)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
