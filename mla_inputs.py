@@ -96,6 +96,21 @@ def normals(key: int, start: int, count: int) -> np.ndarray:
     return out[off:off + count]
 
 
+def normals_parallel(key: int, count: int, chunk: int = 1 << 20) -> np.ndarray:
+    """normals(key, 0, count), computed in chunks on a thread pool (the
+    stream is counter-based, so chunks are independent; identical values)."""
+    out = np.empty(count, np.float64)
+    starts = list(range(0, count, 2 * (chunk // 2)))
+
+    def work(s0):
+        n = min(2 * (chunk // 2), count - s0)
+        out[s0:s0 + n] = normals(key, s0, n)
+
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        list(ex.map(work, starts))
+    return out
+
+
 def uniforms(key: int, start: int, count: int) -> np.ndarray:
     """Uniforms in [0, 1) from the top 53 bits of each draw (float64)."""
     z = draws(key, start, count)
@@ -126,6 +141,19 @@ def store(x: np.ndarray, dtype: str) -> np.ndarray:
     """float64 values -> storage array: float32, or bfloat16 bits (uint16)."""
     x32 = np.asarray(x, dtype=np.float32)
     return x32 if dtype == "f32" else to_bf16_bits(x32)
+
+
+def store_parallel(x: np.ndarray, dtype: str, chunk: int = 1 << 20) -> np.ndarray:
+    """store() of a flat array, in chunks on a thread pool (same values)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    out = np.empty(x.size, np.float32 if dtype == "f32" else np.uint16)
+
+    def work(s0):
+        out[s0:s0 + chunk] = store(x[s0:s0 + chunk], dtype)
+
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        list(ex.map(work, range(0, x.size, chunk)))
+    return out
 
 
 def widen(a: np.ndarray) -> np.ndarray:
@@ -502,7 +530,8 @@ def prolog_inputs(spec: Spec, n_tok: int, hidden: int = PROLOG_HIDDEN, q_rank: i
 
     def draw(name, shape, scale):
         n = int(np.prod(shape))
-        return store((normals(tensor_key(spec.seed, f"{tag}_{name}"), 0, n) * scale).reshape(shape), spec.dtype)
+        return store_parallel(normals_parallel(tensor_key(spec.seed, f"{tag}_{name}"), n) * scale,
+                              spec.dtype).reshape(shape)
 
     return PrologInputs(
         x=draw("x", (n_tok, hidden), 1.0),
