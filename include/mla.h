@@ -267,6 +267,58 @@ mla_status mla_cache_append(const mla_dims* dims, int64_t n_tok, const void* c_k
                             int64_t num_blocks, int32_t block_size, uint32_t* data_err,
                             void* stream);
 
+/* Widths of the fused prolog's projections: the hidden state and the query
+ * latent (the CANN aclnnMlaProlog page's x and c^Q; its tables, which would
+ * give their sizes, are unreadable). */
+typedef struct mla_prolog_dims {
+  int32_t hidden;  /* width of x */
+  int32_t q_rank;  /* width of c^Q */
+} mla_prolog_dims;
+
+/* Workspace bytes mla_prolog needs for n_tok tokens.  Errors: MLA_ERR_NULL,
+ * MLA_ERR_DIMS, MLA_ERR_SHAPE (n_tok < 0), MLA_ERR_UNSUPPORTED (see
+ * mla_prolog). */
+mla_status mla_prolog_workspace_size(const mla_dims* dims, const mla_prolog_dims* pd, int64_t n_tok,
+                                     size_t* bytes);
+
+/* The fused MLA prolog (CANN aclnnMlaProlog: its four paths and formulas),
+ * from the hidden states of n_tok new tokens to their absorbed queries and
+ * their cache rows:
+ *   c^Q  = RmsNorm(x W^DQ)            RmsNorm(y) = gamma * y / sqrt(mean(y^2) + eps)
+ *   q^N  = (c^Q W^UQ) W^UK            per head (W^UK: the absorb step's)
+ *   q^R  = ROPE(c^Q W^QR)             at positions[n]
+ *   q_abs[n][h] = [q^N | q^R]          (what mla_decode_attention reads)
+ *   cache row slot_mapping[n] <- [RmsNorm(x W^DKV) | ROPE(x W^KR)]
+ * The cache write is mla_cache_append's (slots, padding -1, out-of-range
+ * slots reported in *data_err); the last step is mla_absorb_q's.
+ *
+ * x [n_tok][hidden]; weights stored [out][in]: w_dq [q_rank][hidden],
+ * w_dkv [kv_rank][hidden], w_kr [d_rope][hidden], w_uq [n_head d_nope][q_rank]
+ * and w_qr [n_head d_rope][q_rank] (output feature h * width + j), w_uk
+ * [n_head][d_nope][kv_rank]; gamma_q [q_rank], gamma_kv [kv_rank] or NULL
+ * (ones); all of type dt, which must be MLA_BF16.  x and the projection
+ * weights must be 16-byte aligned.  positions int32 [n_tok], slot_mapping
+ * int64 [n_tok], kv_cache [num_blocks][16][kv_rank + d_rope] type kv_dt,
+ * q_abs [n_tok][n_head][kv_rank + d_rope] type q_dt, data_err as in
+ * mla_cache_append (NULL to ignore).  Intermediates (c^Q, the cache
+ * inputs, q^C, q^R) are bf16 in the workspace; products and norms
+ * accumulate in float32.  Asynchronous on `stream`; the workspace must not
+ * be shared with a concurrent call.
+ * Errors: those of mla_prolog_workspace_size, MLA_ERR_UNSUPPORTED (dt not
+ * bf16, hidden or q_rank not a multiple of 32, q_rank > 4096, kv_rank,
+ * d_rope, n_head d_nope or n_head d_rope not a multiple of 16, d_nope not a
+ * multiple of 8, block_size != 16, d_rope > 256), MLA_ERR_ARG (eps, rope
+ * base or style, dtype codes, misaligned x or weights), MLA_ERR_SHAPE
+ * (num_blocks < 1, n_tok > 65535), MLA_ERR_WORKSPACE, MLA_ERR_HIP. */
+mla_status mla_prolog(const mla_dims* dims, const mla_prolog_dims* pd, int64_t n_tok, const void* x,
+                      const void* w_dq, const void* w_uq, const void* w_qr, const void* w_uk,
+                      const void* w_dkv, const void* w_kr, const void* gamma_q, const void* gamma_kv,
+                      mla_dtype dt, float eps_q, float eps_kv, const int32_t* positions,
+                      double rope_base, int32_t rope_style, const int64_t* slot_mapping,
+                      void* kv_cache, mla_dtype kv_dt, int64_t num_blocks, int32_t block_size,
+                      void* q_abs, mla_dtype q_dt, uint32_t* data_err, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Naive-form (multi-head) attention for prefill and chunked prefill over the
  * paged latent cache (memra mla.rs, mla_attend_naive, and the MlaInputs causal
  * rule).  For request b, new query i < t_q and head h, with L = seq_lens[b]

@@ -8,7 +8,8 @@ attention over the paged latent cache plus the LSE-weighted merge) and
 into the paged cache and rotates the query rope part; ``mla_prefill_attention``
 runs the naive (multi-head) form for prefill and chunked prefill;
 ``mla_decode_attention_dcp`` runs one rank's share of context-parallel decode
-and ``mla_lse_combine`` merges the ranks' shares.  See include/mla.h for the
+and ``mla_lse_combine`` merges the ranks' shares; ``mla_prolog`` is the fused
+prolog from hidden states to absorbed queries and cache rows.  See include/mla.h for the
 contract of every entry point.
 """
 from ._binding import (  # noqa: F401
@@ -39,5 +40,8 @@ from ._binding import (  # noqa: F401
     mla_lse_combine,
     mla_prefill_attention,
     mla_prefill_workspace_size,
+    mla_prolog,
+    mla_prolog_dims,
+    mla_prolog_workspace_size,
     mla_status_string,
 )

@@ -25,7 +25,8 @@ MLA_ROPE_NEOX, MLA_ROPE_INTERLEAVED = 0, 1
 EXPORTS = ("mla_default_scale", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode_resolve_splits", "mla_decode_attention", "mla_decompress_v",
            "mla_decode_status", "mla_status_string", "mla_cache_append", "mla_prefill_workspace_size",
-           "mla_prefill_attention", "mla_decode_attention_dcp", "mla_lse_combine")
+           "mla_prefill_attention", "mla_decode_attention_dcp", "mla_lse_combine", "mla_prolog_workspace_size",
+           "mla_prolog")
 
 
 class MlaError(RuntimeError):
@@ -71,6 +72,12 @@ def lib():
                                            i32, i32, i32, vp, ctypes.c_int, vp, vp, sz, i32, vp]
     L.mla_lse_combine.restype = ctypes.c_int
     L.mla_lse_combine.argtypes = [i32, i64, i32, vp, vp, vp, ctypes.c_int, vp, vp]
+    L.mla_prolog_workspace_size.restype = ctypes.c_int
+    L.mla_prolog_workspace_size.argtypes = [P, ctypes.POINTER(mla_prolog_dims), i64, ctypes.POINTER(sz)]
+    L.mla_prolog.restype = ctypes.c_int
+    L.mla_prolog.argtypes = [P, ctypes.POINTER(mla_prolog_dims), i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                             ctypes.c_int, f32, f32, vp, ctypes.c_double, i32, vp, vp, ctypes.c_int, i64, i32, vp,
+                             ctypes.c_int, vp, vp, sz, vp]
     L.mla_decompress_v.restype = ctypes.c_int
     L.mla_decompress_v.argtypes = [P, i64, vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp]
     L.mla_decode_status.restype = ctypes.c_int
@@ -209,6 +216,35 @@ def mla_lse_combine(o_parts, lse_parts, out, lse_out=None, stream=None) -> None:
     width = o_parts.numel() // max(1, P * n)
     _check("mla_lse_combine", lib().mla_lse_combine(int(width), int(n), P, _ptr(o_parts), _ptr(lse_parts), _ptr(out),
                                                     _dt(out), _ptr(lse_out), _stream(stream)))
+
+
+class mla_prolog_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("q_rank", ctypes.c_int32)]
+
+
+def mla_prolog_workspace_size(dims: DimsLike, hidden: int, q_rank: int, n_tok: int) -> int:
+    d = as_dims(dims)
+    pd = mla_prolog_dims(hidden, q_rank)
+    out = ctypes.c_size_t(0)
+    _check("mla_prolog_workspace_size", lib().mla_prolog_workspace_size(ctypes.byref(d), ctypes.byref(pd), int(n_tok),
+                                                                        ctypes.byref(out)))
+    return int(out.value)
+
+
+def mla_prolog(dims: DimsLike, x, w_dq, w_uq, w_qr, w_uk, w_dkv, w_kr, gamma_q, gamma_kv, eps_q: float, eps_kv: float,
+               positions, rope_base: float, rope_style: int, slot_mapping, kv_cache, q_abs, workspace, data_err=None,
+               stream=None) -> None:
+    """Fused prolog: x [n_tok][hidden] and the [out][in] projection weights
+    -> q_abs [n_tok][H][kv_rank + d_rope] and the cache rows slot_mapping[n]."""
+    d = as_dims(dims)
+    n_tok, hidden = int(x.shape[0]), int(x.shape[1])
+    pd = mla_prolog_dims(hidden, int(w_dq.shape[0]))
+    _check("mla_prolog", lib().mla_prolog(
+        ctypes.byref(d), ctypes.byref(pd), n_tok, _ptr(x), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(w_uk), _ptr(w_dkv),
+        _ptr(w_kr), _ptr(gamma_q), _ptr(gamma_kv), _dt(x), float(eps_q), float(eps_kv), _ptr(positions),
+        float(rope_base), int(rope_style), _ptr(slot_mapping), _ptr(kv_cache), _dt(kv_cache), int(kv_cache.shape[0]),
+        int(kv_cache.shape[1]), _ptr(q_abs), _dt(q_abs), _ptr(data_err), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def mla_decompress_v(dims: DimsLike, o_lat, w_uv, out, stream=None) -> None:

@@ -89,6 +89,45 @@ struct CacheAppend {
 
 hipError_t launch_cache_append(const CacheAppend& c, hipStream_t stream);
 
+// The fused prolog.  Skinny GEMM: part[split][n][o] over the rows o of up to
+// four concatenated weight segments (each [rows][K], rows a multiple of 16).
+struct GemmSeg {
+  const uint16_t* w;
+  int rows;
+};
+struct SkinnyGemm {
+  const uint16_t* x;  // [n_tok][K]
+  GemmSeg seg[4];
+  int n_seg, K, N;    // N = total rows
+  int64_t n_tok;
+  int splits, kper;   // K splits requested / k per split (set by the launcher)
+  float* part;        // [splits][n_tok][N]
+};
+struct PrologArgs {
+  const void *x, *w_dq, *w_uq, *w_qr, *w_uk, *w_dkv, *w_kr, *gamma_q, *gamma_kv;
+  float eps_q, eps_kv;
+  const int32_t* positions;
+  double rope_base;
+  bool interleaved, cache_bf16, q_bf16;
+  const int64_t* slots;
+  void* cache;
+  int64_t num_slots;
+  uint32_t* err;
+  void* q_abs;
+  int64_t n_tok;
+  int hidden, q_rank, n_head, d_nope, d_rope, kv_rank;
+  int splits1, splits2;
+  float* part;                      // workspace: split partials
+  uint16_t *cq, *ckv, *kpe, *qn, *qp;  // workspace: bf16 intermediates
+};
+struct PrologPlan {
+  int splits1, splits2;
+  size_t part_off, cq_off, ckv_off, kpe_off, qn_off, qp_off, bytes;
+};
+PrologPlan prolog_plan(int n_head, int d_nope, int d_rope, int kv_rank, int hidden, int q_rank, int64_t n_tok);
+bool prolog_supported(int n_head, int d_nope, int d_rope, int kv_rank, int hidden, int q_rank);
+hipError_t launch_prolog(const PrologArgs& a, hipStream_t stream);
+
 // One naive-form prefill call.  Workspace: the 256-byte header, one status
 // word per request, then K_nope [B][H][max_rows][d_nope] and V
 // [B][H][max_rows][d_v] (bf16), each 256-byte aligned.

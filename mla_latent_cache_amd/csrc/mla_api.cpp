@@ -378,3 +378,91 @@ mla_status mla_decode_status(const void* workspace, uint32_t* flags, void* strea
 }
 
 }  // extern "C"
+
+extern "C" {
+
+mla_status mla_prolog_workspace_size(const mla_dims* dims, const mla_prolog_dims* pd, int64_t n_tok, size_t* bytes) {
+  if (!dims || !pd || !bytes) return MLA_ERR_NULL;
+  if (dims->n_head < 1 || dims->d_nope < 1 || dims->d_rope < 0 || dims->d_rope % 2 != 0 || dims->kv_rank < 1 ||
+      pd->hidden < 1 || pd->q_rank < 1)
+    return MLA_ERR_DIMS;
+  if (n_tok < 0) return MLA_ERR_SHAPE;
+  if (!mla::prolog_supported(dims->n_head, dims->d_nope, dims->d_rope, dims->kv_rank, pd->hidden, pd->q_rank))
+    return MLA_ERR_UNSUPPORTED;
+  *bytes = mla::prolog_plan(dims->n_head, dims->d_nope, dims->d_rope, dims->kv_rank, pd->hidden, pd->q_rank, n_tok)
+               .bytes;
+  return MLA_OK;
+}
+
+mla_status mla_prolog(const mla_dims* dims, const mla_prolog_dims* pd, int64_t n_tok, const void* x, const void* w_dq,
+                      const void* w_uq, const void* w_qr, const void* w_uk, const void* w_dkv, const void* w_kr,
+                      const void* gamma_q, const void* gamma_kv, mla_dtype dt, float eps_q, float eps_kv,
+                      const int32_t* positions, double rope_base, int32_t rope_style, const int64_t* slot_mapping,
+                      void* kv_cache, mla_dtype kv_dt, int64_t num_blocks, int32_t block_size, void* q_abs,
+                      mla_dtype q_dt, uint32_t* data_err, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const mla_status ws = mla_prolog_workspace_size(dims, pd, n_tok, &need);
+  if (ws != MLA_OK) return ws;
+  if (num_blocks < 1) return MLA_ERR_SHAPE;
+  if (block_size != 16) return MLA_ERR_UNSUPPORTED;
+  if (dims->d_rope > 2 * mla::kRopeTableMax) return MLA_ERR_UNSUPPORTED;
+  if (!dt_ok(dt) || !dt_ok(kv_dt) || !dt_ok(q_dt)) return MLA_ERR_ARG;
+  if (dt != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!(eps_q >= 0.f) || !isfinite(eps_q) || !(eps_kv >= 0.f) || !isfinite(eps_kv)) return MLA_ERR_ARG;
+  if (rope_style != MLA_ROPE_NEOX && rope_style != MLA_ROPE_INTERLEAVED) return MLA_ERR_ARG;
+  if (dims->d_rope > 0 && (!(rope_base > 0.0) || !isfinite(rope_base))) return MLA_ERR_ARG;
+  if (num_blocks > INT64_MAX / block_size) return MLA_ERR_SHAPE;
+  if (!workspace) return MLA_ERR_NULL;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  if (n_tok == 0) return MLA_OK;
+  if (!x || !w_dq || !w_uq || !w_uk || !w_dkv || !slot_mapping || !kv_cache || !q_abs) return MLA_ERR_NULL;
+  if (dims->d_rope > 0 && (!w_qr || !w_kr || !positions)) return MLA_ERR_NULL;
+  // the products read 16-byte runs of x and of every weight row
+  for (const void* ptr : {x, w_dq, w_uq, w_qr, w_dkv, w_kr})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return MLA_ERR_ARG;
+  const mla::PrologPlan p =
+      mla::prolog_plan(dims->n_head, dims->d_nope, dims->d_rope, dims->kv_rank, pd->hidden, pd->q_rank, n_tok);
+  char* wsb = static_cast<char*>(workspace);
+  mla::PrologArgs a = {};
+  a.x = x;
+  a.w_dq = w_dq;
+  a.w_uq = w_uq;
+  a.w_qr = w_qr;
+  a.w_uk = w_uk;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.gamma_q = gamma_q;
+  a.gamma_kv = gamma_kv;
+  a.eps_q = eps_q;
+  a.eps_kv = eps_kv;
+  a.positions = positions;
+  a.rope_base = rope_base;
+  a.interleaved = rope_style == MLA_ROPE_INTERLEAVED;
+  a.cache_bf16 = kv_dt == MLA_BF16;
+  a.q_bf16 = q_dt == MLA_BF16;
+  a.slots = slot_mapping;
+  a.cache = kv_cache;
+  a.num_slots = num_blocks * block_size;
+  a.err = data_err;
+  a.q_abs = q_abs;
+  a.n_tok = n_tok;
+  a.hidden = pd->hidden;
+  a.q_rank = pd->q_rank;
+  a.n_head = dims->n_head;
+  a.d_nope = dims->d_nope;
+  a.d_rope = dims->d_rope;
+  a.kv_rank = dims->kv_rank;
+  a.splits1 = p.splits1;
+  a.splits2 = p.splits2;
+  a.part = reinterpret_cast<float*>(wsb + p.part_off);
+  a.cq = reinterpret_cast<uint16_t*>(wsb + p.cq_off);
+  a.ckv = reinterpret_cast<uint16_t*>(wsb + p.ckv_off);
+  a.kpe = reinterpret_cast<uint16_t*>(wsb + p.kpe_off);
+  a.qn = reinterpret_cast<uint16_t*>(wsb + p.qn_off);
+  a.qp = reinterpret_cast<uint16_t*>(wsb + p.qp_off);
+  const hipError_t e = mla::launch_prolog(a, static_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidValue) return MLA_ERR_SHAPE;
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"
