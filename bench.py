@@ -280,6 +280,65 @@ def time_dcp(spec, case, dims, q_abs, stream, world: int = 8, interleave: int = 
     }
 
 
+def time_mlaprolog(spec, case, dims, reps: int = 20):
+    """The fused prolog for the decode step's new tokens (one per request and
+    query), timed with HIP events: hidden states -> absorbed queries and cache
+    rows, at hidden and q_rank widths of the mla_inputs defaults."""
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_latent_cache_amd as mla
+
+    n_tok = spec.batch * spec.t_q
+    hid, qr = mi.PROLOG_HIDDEN, mi.PROLOG_Q_RANK
+    p = mi.prolog_inputs(spec, n_tok, hid, qr, tag="bench_prolog")
+
+    def dev(a):
+        if a is None or a.size == 0:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    ap = mi.step_append(spec, case.seq_lens, case.block_table)
+    H, D, e = spec.n_head, spec.D, 2
+    cache = torch.zeros(case.num_blocks, 16, D, dtype=torch.bfloat16, device="cuda")
+    q_abs = torch.empty(n_tok, H, D, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.mla_prolog_workspace_size(dims, hid, qr, n_tok), dtype=torch.uint8, device="cuda")
+    args = [dev(p.x), dev(p.w_dq), dev(p.w_uq), dev(p.w_qr), dev(case.w_uk), dev(p.w_dkv), dev(p.w_kr),
+            dev(p.gamma_q), dev(p.gamma_kv)]
+    pos = torch.from_numpy(ap.positions).cuda()
+    slots = torch.from_numpy(ap.slots).cuda()
+    stream = torch.cuda.current_stream()
+
+    def call():
+        mla.mla_prolog(dims, *args, mi.RMS_EPS, mi.RMS_EPS, pos, mi.ROPE_BASE, mla.MLA_ROPE_NEOX, slots, cache, q_abs,
+                       ws, None, stream)
+
+    for _ in range(3):
+        call()
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in es:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in es) / reps * 1e-3
+    w_bytes = (qr * hid + spec.kv_rank * hid + spec.d_rope * hid + H * (spec.d_nope + spec.d_rope) * qr
+               + H * spec.d_nope * spec.kv_rank + qr + spec.kv_rank) * e
+    io_bytes = n_tok * hid * e + n_tok * H * D * e + n_tok * D * e + n_tok * (4 + 8)
+    byts = w_bytes + io_bytes
+    return {
+        "kernels": "skinny_gemm x2 (split-K MFMA), prolog_finish1/2, cache_append_kernel, absorb_mfma",
+        "tokens": n_tok,
+        "hidden": hid,
+        "q_rank": qr,
+        "call_us": round(t * 1e6, 2),
+        "algorithmic_bytes": byts,
+        "gbs": round(byts / t / 1e9, 1),
+        "frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def prefill_figures(spec, seq_lens):
     """Algorithmic work of one naive-form prefill call: flops of the
     decompression GEMM (every cache row of a request through W_UK and W_UV)
@@ -369,6 +428,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the naive-form prefill measurement")
     ap.add_argument("--no-dcp", action="store_true", help="skip the context-parallel share measurement")
+    ap.add_argument("--no-mlaprolog", action="store_true", help="skip the fused prolog measurement")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel of a timed step from the host instead of replaying a HIP graph")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -508,6 +568,8 @@ def main() -> int:
     prefill = None if args.no_prefill else time_prefill()
     dcp = time_dcp(spec, case, dims, copies[0]["q_abs"], stream) if (spec.name == "glm52_decode" and not args.no_dcp) \
         else None
+    mlaprolog = time_mlaprolog(spec, case, dims) if (not spec.q_given and spec.dtype == "bf16"
+                                                     and not args.no_mlaprolog) else None
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -548,6 +610,7 @@ def main() -> int:
         "prolog": prolog,
         "prefill": prefill,
         "dcp": dcp,
+        "mlaprolog": mlaprolog,
         "roofline": {
             "kernel": "decode call: decode_split_mfma + decode_merge",
             "bound": "hbm",

@@ -119,10 +119,11 @@ struct PrologArgs {
   int splits1, splits2;
   float* part;                      // workspace: split partials
   uint16_t *cq, *ckv, *kpe, *qn, *qp;  // workspace: bf16 intermediates
+  float* yq;                        // workspace: x W^DQ before its norm
 };
 struct PrologPlan {
   int splits1, splits2;
-  size_t part_off, cq_off, ckv_off, kpe_off, qn_off, qp_off, bytes;
+  size_t part_off, cq_off, ckv_off, kpe_off, qn_off, qp_off, yq_off, bytes;
 };
 PrologPlan prolog_plan(int n_head, int d_nope, int d_rope, int kv_rank, int hidden, int q_rank, int64_t n_tok);
 bool prolog_supported(int n_head, int d_nope, int d_rope, int kv_rank, int hidden, int q_rank);

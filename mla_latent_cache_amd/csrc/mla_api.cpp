@@ -460,6 +460,7 @@ mla_status mla_prolog(const mla_dims* dims, const mla_prolog_dims* pd, int64_t n
   a.kpe = reinterpret_cast<uint16_t*>(wsb + p.kpe_off);
   a.qn = reinterpret_cast<uint16_t*>(wsb + p.qn_off);
   a.qp = reinterpret_cast<uint16_t*>(wsb + p.qp_off);
+  a.yq = reinterpret_cast<float*>(wsb + p.yq_off);
   const hipError_t e = mla::launch_prolog(a, static_cast<hipStream_t>(stream));
   if (e == hipErrorInvalidValue) return MLA_ERR_SHAPE;
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -81,36 +81,50 @@ __device__ __forceinline__ float load_gain(const void* gamma, bool bf16, int i) 
   return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(gamma)[i]) : static_cast<const float*>(gamma)[i];
 }
 
-// Finish 1, one workgroup per token: sum the split partials of x W^DQ,
-// x W^DKV and x W^KR; RmsNorm the first (gamma_q, eps_q, float32) into c^Q;
-// the other two go to the cache append as they are.  All bf16.
-constexpr int kFinishPerThread = 16;  // q_rank <= 256 * 16
+// Sum over the split partials of one output column (the splits in order,
+// loads eight at a time so the row costs a few memory latencies).
+__device__ __forceinline__ float sum_splits(const float* p, int64_t sstride, int splits) {
+  float v = 0.f;
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t[k] = p[(s + k) * sstride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v += t[k];
+  }
+  for (; s < splits; ++s) v += p[s * sstride];
+  return v;
+}
+
+// Finish 1, one thread per (token, column): the sums of x W^DQ go to the
+// float32 row the norm reads; those of x W^DKV and x W^KR go to the cache
+// append as they are (bf16).
 __global__ __launch_bounds__(256) void prolog_finish1(const PrologArgs a) {
+  const int64_t n = blockIdx.y;
+  const int N = a.q_rank + a.kv_rank + a.d_rope;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= N) return;
+  const float v = sum_splits(a.part + n * N + c, a.n_tok * (int64_t)N, a.splits1);
+  if (c < a.q_rank) a.yq[n * a.q_rank + c] = v;
+  else if (c < a.q_rank + a.kv_rank) a.ckv[n * a.kv_rank + (c - a.q_rank)] = f32_to_bf16(v);
+  else a.kpe[n * a.d_rope + (c - a.q_rank - a.kv_rank)] = f32_to_bf16(v);
+}
+
+// c^Q = RmsNorm(x W^DQ) per token (gamma_q, eps_q; float32), stored bf16.
+constexpr int kFinishPerThread = 16;  // q_rank <= 256 * 16
+__global__ __launch_bounds__(256) void prolog_norm_q(const PrologArgs a) {
   const int64_t n = blockIdx.x;
   const int tid = threadIdx.x;
-  const int N = a.q_rank + a.kv_rank + a.d_rope;
-  const float* p = a.part + n * N;
-  const int64_t sstride = a.n_tok * (int64_t)N;
+  const float* y = a.yq + n * a.q_rank;
   float qv[kFinishPerThread];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kFinishPerThread; ++j) {
     const int c = tid + 256 * j;
-    qv[j] = 0.f;
-    if (c < a.q_rank) {
-      float v = 0.f;
-      for (int s = 0; s < a.splits1; ++s) v += p[s * sstride + c];
-      qv[j] = v;
-      ss += v * v;
-    }
+    qv[j] = c < a.q_rank ? y[c] : 0.f;
+    ss += qv[j] * qv[j];
   }
-  for (int c = a.q_rank + tid; c < N; c += 256) {
-    float v = 0.f;
-    for (int s = 0; s < a.splits1; ++s) v += p[s * sstride + c];
-    if (c < a.q_rank + a.kv_rank) a.ckv[n * a.kv_rank + (c - a.q_rank)] = f32_to_bf16(v);
-    else a.kpe[n * a.d_rope + (c - a.q_rank - a.kv_rank)] = f32_to_bf16(v);
-  }
-  // Block sum of squares of the c^Q row.
   __shared__ float red[4];
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -131,10 +145,7 @@ __global__ __launch_bounds__(256) void prolog_finish2(const PrologArgs a) {
   const int NQ = a.n_head * a.d_nope, N = NQ + a.n_head * a.d_rope;
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= N) return;
-  const float* p = a.part + n * N + c;
-  const int64_t sstride = a.n_tok * (int64_t)N;
-  float v = 0.f;
-  for (int s = 0; s < a.splits2; ++s) v += p[s * sstride];
+  const float v = sum_splits(a.part + n * N + c, a.n_tok * (int64_t)N, a.splits2);
   if (c < NQ) a.qn[n * NQ + c] = f32_to_bf16(v);
   else a.qp[n * (N - NQ) + (c - NQ)] = f32_to_bf16(v);
 }
@@ -181,7 +192,8 @@ PrologPlan prolog_plan(int n_head, int d_nope, int d_rope, int kv_rank, int hidd
   p.kpe_off = al(p.ckv_off + (size_t)n_tok * kv_rank * 2);
   p.qn_off = al(p.kpe_off + (size_t)n_tok * d_rope * 2);
   p.qp_off = al(p.qn_off + (size_t)n_tok * n_head * d_nope * 2);
-  p.bytes = al(p.qp_off + (size_t)n_tok * n_head * d_rope * 2);
+  p.yq_off = al(p.qp_off + (size_t)n_tok * n_head * d_rope * 2);
+  p.bytes = al(p.yq_off + (size_t)n_tok * q_rank * 4);
   if (p.bytes == 0) p.bytes = 256;
   return p;
 }
@@ -193,7 +205,7 @@ bool prolog_supported(int n_head, int d_nope, int d_rope, int kv_rank, int hidde
 
 hipError_t launch_prolog(const PrologArgs& a, hipStream_t stream) {
   if (a.n_tok == 0) return hipSuccess;
-  if (a.n_tok > 65535) return hipErrorInvalidValue;  // grid rows of the second finish kernel
+  if (a.n_tok > 65535) return hipErrorInvalidValue;  // grid rows of the finish kernels
   // 1: x [W^DQ; W^DKV; W^KR]^T
   SkinnyGemm g1 = {};
   g1.x = static_cast<const uint16_t*>(a.x);
@@ -208,7 +220,10 @@ hipError_t launch_prolog(const PrologArgs& a, hipStream_t stream) {
   g1.part = a.part;
   hipError_t e = launch_skinny(g1, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prolog_finish1, dim3((unsigned)a.n_tok), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(prolog_finish1, dim3((unsigned)((g1.N + 255) / 256), (unsigned)a.n_tok), dim3(256), 0, stream,
+                     a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(prolog_norm_q, dim3((unsigned)a.n_tok), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 2: c^Q [W^UQ; W^QR]^T
   SkinnyGemm g2 = {};
