@@ -12,9 +12,12 @@
  *
  * and, upstream of step 2, the cache-append prolog mla_cache_append (RmsNorm
  * of the new latent rows, rope of their k_pe and of the query rope part, and
- * the slot-mapped write into the paged cache).  For prefill and chunked
- * prefill, mla_prefill_attention runs the naive (multi-head) form over the
- * same paged cache.
+ * the slot-mapped write into the paged cache), and the whole fused prolog
+ * mla_prolog (hidden states to absorbed queries and cache rows).  For prefill
+ * and chunked prefill, mla_prefill_attention runs the naive (multi-head) form
+ * over the same paged cache.  For context-parallel decode,
+ * mla_decode_attention_dcp runs one rank's share and mla_lse_combine merges
+ * the ranks' shares.
  *
  * Pages this interface follows (cited by title and section):
  *   memra-engine 0.124.0 source page "mla.rs": MlaDims (geometry), MlaDims::scale,
