@@ -22,54 +22,71 @@ namespace mla {
 namespace {
 
 constexpr int kTokTile = 64;  // tokens per workgroup pass (four MFMA column tiles)
-constexpr int kKBatch = 4;    // k-steps of 32 whose loads go out before their products
+constexpr int kKBatch = 4;    // k-steps of 32 per batch of activation loads
+constexpr int kKChunk = 16;   // k-steps of 32 per chunk: weight loads in flight and LDS-staged activations
 
 // part[split][n][o] = sum over this split's k of x[n][k] * W[o][k], for the
 // rows o of the concatenated segments.  Each wave takes 16 rows (one
-// segment) and all of the workgroup's tokens.
+// segment) and the workgroup's tokens, NT tiles of 16 (registers sized to the
+// tiles in use).  Per chunk of kKChunk k-steps the wave's weight loads go out
+// first (HBM); meanwhile the workgroup stages its tokens' activations for
+// the chunk in LDS once (rows XOR-swizzled by row % 16 in 16-byte units, so
+// the operand reads are free of bank conflicts) instead of every wave
+// reading them from L2.
+template <int NT>
 __global__ __launch_bounds__(256) void skinny_gemm(const SkinnyGemm g) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int CH = 4 * kKChunk;  // 16-byte chunks of a staged row (kKChunk k-steps of 32)
+  __shared__ __attribute__((aligned(16))) u32x4 xs[16 * NT][CH];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
   const int o0 = blockIdx.x * 64 + 16 * w;  // first output row of the wave
-  if (o0 >= g.N) return;                    // whole wave; the kernel has no barriers
+  const bool active = o0 < g.N;             // (the workgroup's barriers need every wave)
   int si = 0, base = 0;
   while (si + 1 < g.n_seg && o0 >= base + g.seg[si].rows) base += g.seg[si++].rows;
-  const uint16_t* wrow = g.seg[si].w + (int64_t)(o0 - base + l16) * g.K + 8 * grp;
+  const uint16_t* wrow = g.seg[si].w + (int64_t)((active ? o0 - base : 0) + l16) * g.K + 8 * grp;
   const int k0 = blockIdx.y * g.kper;
   const int k1 = k0 + g.kper < g.K ? k0 + g.kper : g.K;
   const int64_t t0 = (int64_t)blockIdx.z * kTokTile;
-  const int nt = g.n_tok - t0 >= kTokTile ? 4 : (int)((g.n_tok - t0 + 15) / 16);  // token tiles in use
-  const uint16_t* xrow[4];
-  bool tok_ok[4];
+  const int nt = g.n_tok - t0 >= 16 * NT ? NT : (int)((g.n_tok - t0 + 15) / 16);  // token tiles in use
+  f32x4 acc[NT];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int64_t tok = t0 + 16 * tt + l16;
-    tok_ok[tt] = tok < g.n_tok;
-    xrow[tt] = g.x + (tok_ok[tt] ? tok : 0) * g.K + 8 * grp;
-  }
-  f32x4 acc[4];
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kc = k0; kc < k1; kc += 32 * kKChunk) {
+    u32x4 a[kKChunk];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = k0; k < k1; k += 32 * kKBatch) {
-    u32x4 a[kKBatch], b[kKBatch][4];
-#pragma unroll
-    for (int u = 0; u < kKBatch; ++u) {
-      const bool in = k + 32 * u < k1;
-      a[u] = in ? *reinterpret_cast<const u32x4*>(wrow + k + 32 * u) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        b[u][tt] = in && tt < nt && tok_ok[tt] ? *reinterpret_cast<const u32x4*>(xrow[tt] + k + 32 * u)
-                                               : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < kKChunk; ++u)
+      a[u] = active && kc + 32 * u < k1 ? *reinterpret_cast<const u32x4*>(wrow + kc + 32 * u)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    // Stage x[t0 + r][kc + 8 c .. + 7] at xs[r][c ^ (r % 16)] (zeros past the
+    // tokens or the split).
+    for (int i = tid; i < 16 * NT * CH; i += 256) {
+      const int r = i / CH, c = i - r * CH;
+      const int64_t tok = t0 + r;
+      const int k = kc + 8 * c;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (tok < g.n_tok && k < k1) v = *reinterpret_cast<const u32x4*>(g.x + tok * g.K + k);
+      xs[r][c ^ (r & 15)] = v;
     }
+    __syncthreads();
+    if (active) {
 #pragma unroll
-    for (int u = 0; u < kKBatch; ++u)
+      for (int u = 0; u < kKChunk; ++u) {
+        if (kc + 32 * u >= k1) break;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        if (tt < nt) acc[tt] = mfma16x16x32(as_bf16x8(a[u]), as_bf16x8(b[u][tt]), acc[tt]);
+        for (int tt = 0; tt < NT; ++tt) {
+          if (tt >= nt) continue;
+          const int r = 16 * tt + l16;
+          const u32x4 b = xs[r][(4 * u + grp) ^ (r & 15)];
+          acc[tt] = mfma16x16x32(as_bf16x8(a[u]), as_bf16x8(b), acc[tt]);
+        }
+      }
+    }
+    __syncthreads();  // the staging area is refilled for the next chunk
   }
+  if (!active) return;
   // Lane (l16, grp) holds token column l16 of each tile and rows 4 grp .. + 3.
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
+  for (int tt = 0; tt < NT; ++tt) {
     const int64_t tok = t0 + 16 * tt + l16;
     if (tt < nt && tok < g.n_tok)
       *reinterpret_cast<f32x4*>(g.part + ((int64_t)blockIdx.y * g.n_tok + tok) * g.N + o0 + 4 * grp) = acc[tt];
@@ -168,7 +185,11 @@ hipError_t launch_skinny(const SkinnyGemm& g0, hipStream_t stream) {
   const int kb = 32 * kKBatch;
   g.kper = ((g.K + g.splits - 1) / g.splits + kb - 1) / kb * kb;
   const dim3 grid((g.N + 63) / 64, (g.K + g.kper - 1) / g.kper, (unsigned)((g.n_tok + kTokTile - 1) / kTokTile));
-  hipLaunchKernelGGL(skinny_gemm, grid, dim3(256), 0, stream, g);
+  // token tiles per pass: all four once a pass is full, else just those in use
+  const int64_t t = g.n_tok >= kTokTile ? 4 : (g.n_tok + 15) / 16;
+  if (t <= 1) hipLaunchKernelGGL(skinny_gemm<1>, grid, dim3(256), 0, stream, g);
+  else if (t == 2) hipLaunchKernelGGL(skinny_gemm<2>, grid, dim3(256), 0, stream, g);
+  else hipLaunchKernelGGL(skinny_gemm<4>, grid, dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
