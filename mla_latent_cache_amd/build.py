@@ -27,11 +27,18 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Per-source additions.  The prefill attention kernel keeps 128 accumulator
+# registers across its tile loop and rescales them (vector work) on a rare
+# branch; with the matrix-register form of the MFMA the compiler copies all of
+# them to vector registers on every tile (about a quarter of the loop's
+# instructions).  The vector-register form keeps them where the vector unit
+# can reach them, with bitwise-identical results.
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    cmd = [HIPCC, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + EXTRA_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
