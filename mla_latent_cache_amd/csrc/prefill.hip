@@ -194,7 +194,8 @@ __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a
 // ---------------------------------------------------------------------------
 // Causal flash attention over the decompressed rows
 // ---------------------------------------------------------------------------
-constexpr int kAQ = 128;     // queries per workgroup (32 per wave)
+constexpr int kAQ = 128;     // queries per workgroup (128 / NW per wave)
+constexpr int kAW = 8;       // waves per attention workgroup
 constexpr int kAT = 32;      // cache rows per tile
 constexpr int kAStages = 4;  // tile ring: three tiles in flight while one is used
 
@@ -254,13 +255,19 @@ __device__ __forceinline__ void lgkm_wait(uint2& x, uint2& y) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N) : "memory");
 }
 
-template <int DR>
-__global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
+// NW waves per workgroup: with four, each wave owns 32 queries (two query
+// tiles) and has a SIMD to itself; with eight, 16 queries each and two waves
+// per SIMD, so that one wave's softmax and LDS waits overlap the other's
+// matrix products (the register budget halves to 256).
+template <int DR, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_attend(const PrefillArgs a) {
   using T = ATile<DR>;
   using G = PGeom<DR>;
   constexpr int DN = T::DN, DV = T::DV, D = G::D;
+  constexpr int QPW = kAQ / NW, NQT = QPW / 16;  // queries and 16-query tiles per wave
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ __attribute__((aligned(16))) u32x4 stage[kAStages][T::STAGE];
-  __shared__ uint32_t wflags[4];
+  __shared__ uint32_t wflags[NW];
 
   // Workgroup i runs on XCD i % 8: the query tiles of one (request, head)
   // take consecutive slots of one XCD, so they stream the same decompressed
@@ -286,12 +293,12 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
   const int n_tiles = vis_end > 0 ? (int)((vis_end + kAT - 1) / kAT) : 0;
 
   // Queries: B operand of S^T = K Q^T.  Lane (l16, g) of query tile n holds
-  // query i = i0 + 32 w + 16 n + l16, dims 32 ks + 8 g .. + 7.
-  bf16x8 qf[2][T::KSTEPS];
-  int qi[2];
+  // query i = i0 + QPW w + 16 n + l16, dims 32 ks + 8 g .. + 7.
+  bf16x8 qf[NQT][T::KSTEPS];
+  int qi[NQT];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    qi[n] = i0 + 32 * w + 16 * n + l16;
+  for (int n = 0; n < NQT; ++n) {
+    qi[n] = i0 + QPW * w + 16 * n + l16;
     const bool ok = qi[n] < t_q;
     const int64_t row = ((int64_t)b * t_q + (ok ? qi[n] : 0)) * H + h;
 #pragma unroll
@@ -310,15 +317,19 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
   // Tile loads.  Load u of a stage fills chunks [64 u, 64 u + 64): loads
   // [0, KN_LOADS) the K_nope rows (pitch KN_P), then KP_HALF loads per 16-row
   // block of k_pe (pitch KP_P), then the V rows (pitch V_P).  Wave w issues
-  // loads u = w + 4 j; the lane offsets do not depend on the tile.
+  // loads u = w + NW j (with four waves every round is whole, pads included;
+  // with eight, the USED loads only, so wave 0 issues one more than the
+  // others); the lane offsets do not depend on the tile.
+  constexpr int NLD = NW == 4 ? T::LPW : (T::USED + NW - 1) / NW;  // loads of the busiest wave
+  const bool full_w = NW == 4 || w < T::USED - NW * (NLD - 1);     // this wave issues NLD loads
   const uint16_t* kw = a.kw + ((int64_t)b * H + h) * a.max_rows * DN;
   const uint16_t* vw = a.vw + ((int64_t)b * H + h) * a.max_rows * DV;
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
   constexpr uint32_t kOut = 0x40000000u;  // beyond any buffer range: loads zeros
-  uint32_t voffs[T::LPW];
+  uint32_t voffs[NLD];
 #pragma unroll
-  for (int j = 0; j < T::LPW; ++j) {
-    const int u = w + 4 * j, q = 64 * u + lane;
+  for (int j = 0; j < NLD; ++j) {
+    const int u = w + NW * j, q = 64 * u + lane;
     uint32_t v = kOut;
     if (u < T::KN_LOADS) {
       const int r = q / T::KN_P, p = q - r * T::KN_P;  // slot p of row r holds chunk p ^ swizzle(r)
@@ -355,9 +366,11 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
     const i32x4 rs_v = raw_rsrc(vw + (int64_t)j0 * DV, (uint32_t)(nval * DV * 2));
     i32x4 rs_p = rs_v;
     if constexpr (DR > 0) {
-      // k_pe of this wave's block (the fourth load round: wave w takes block
-      // w / KP_HALF); row r of a block at byte r * D * 2 from its column 512.
-      const int hb = w / T::KP_HALF;
+      // k_pe of the block of this wave's k_pe load (if it has one: the first
+      // of its loads at or past KN_LOADS); row r of a block at byte r * D * 2
+      // from its column 512.
+      const int up = w + NW * ((T::KN_LOADS - w + NW - 1) / NW);
+      const int hb = up < T::KN_LOADS + T::KP_LOADS ? (up - T::KN_LOADS) / T::KP_HALF : 0;
       const int nv = nval - 16 * hb <= 0 ? 0 : (nval - 16 * hb >= 16 ? 16 : nval - 16 * hb);
       const int32_t bid = hb ? id[1] : id[0];
       const bool ok = (uint32_t)bid < nb32;
@@ -368,20 +381,43 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
     }
     const uint32_t base = lds_addr(stage[buf]);
 #pragma unroll
-    for (int j = 0; j < T::LPW; ++j) {
-      const i32x4 rs = T::region(j) == 0 ? rs_k : (T::region(j) == 1 ? rs_p : rs_v);
-      dma16(rs, base + 1024u * (uint32_t)(w + 4 * j), voffs[j]);
+    for (int j = 0; j < NLD; ++j) {
+      const int u = w + NW * j;
+      if constexpr (NW == 4) {
+        const i32x4 rs = T::region(j) == 0 ? rs_k : (T::region(j) == 1 ? rs_p : rs_v);
+        dma16(rs, base + 1024u * (uint32_t)u, voffs[j]);
+      } else if (j < NLD - 1 || full_w) {
+        const i32x4 rs = u < T::KN_LOADS ? rs_k : (u < T::KN_LOADS + T::KP_LOADS ? rs_p : rs_v);
+        dma16(rs, base + 1024u * (uint32_t)u, voffs[j]);
+      }
     }
   };
+  // Wait until at most K tiles' loads of this wave are outstanding.
+  auto wait_tiles = [&](auto k_tiles) {
+    constexpr int K = decltype(k_tiles)::value;
+    if constexpr (NW == 4) {
+      wait_vmcnt<K * NLD>();
+    } else {
+      if (full_w) wait_vmcnt<K * NLD>();
+      else wait_vmcnt<K * (NLD - 1)>();
+    }
+  };
+  using tiles0 = std::integral_constant<int, 0>;
+  using tiles1 = std::integral_constant<int, 1>;
+  using tiles2 = std::integral_constant<int, 2>;
 
-  f32x4 acc[DV / 16][2];
+  f32x4 acc[DV / 16][NQT];
 #pragma unroll
-  for (int c = 0; c < DV / 16; ++c) acc[c][0] = acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m2[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  for (int c = 0; c < DV / 16; ++c)
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) acc[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2[NQT], lsum[NQT];
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) m2[n] = -INFINITY, lsum[n] = 0.f;
   const float sl2 = a.scale * kLog2e;
-  int horizon[2];  // last visible row of each query (inclusive)
+  int horizon[NQT];  // last visible row of each query (inclusive)
 #pragma unroll
-  for (int n = 0; n < 2; ++n) horizon[n] = qi[n] < t_q ? (int)(L - t_q + qi[n]) : -1;
+  for (int n = 0; n < NQT; ++n) horizon[n] = qi[n] < t_q ? (int)(L - t_q + qi[n]) : -1;
 
   // Lane bases of the operand reads within a stage (bytes).
   //   K (A of S^T), rows 16 kt + l16, dims 32 ks + 8 g: K_nope for
@@ -404,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
   static_assert(NS > kA && kA < 16, "read-ahead must fit the LDS counter");
   // The S step I also runs piece I of the caller's work (the softmax of the
   // previous tile), so that the vector ALU works while the matrix cores do.
-  auto s_tile = [&](uint32_t sb, f32x4 (&sp)[2][2], auto&& piece) {
+  auto s_tile = [&](uint32_t sb, f32x4 (&sp)[2][NQT], auto&& piece) {
     u32x4 kr[NS];
     auto rd = [&]<int I>() {
       constexpr int ks = I / 2, kt = I % 2;
@@ -416,15 +452,17 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
     [&]<int... I>(std::integer_sequence<int, I...>) { (rd.template operator()<I>(), ...); }(
         std::make_integer_sequence<int, kA>{});
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) sp[kt][0] = sp[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) sp[kt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (([&] {
          constexpr int ks = I / 2, kt = I % 2;
          constexpr int issued = I + kA < NS ? I + kA : NS;
          lgkm_wait<issued - 1 - I>(kr[I]);
          const bf16x8 kA_ = as_bf16x8(kr[I]);
-         sp[kt][0] = mfma16x16x32(kA_, qf[0][ks], sp[kt][0]);
-         sp[kt][1] = mfma16x16x32(kA_, qf[1][ks], sp[kt][1]);
+#pragma unroll
+         for (int n = 0; n < NQT; ++n) sp[kt][n] = mfma16x16x32(kA_, qf[n][ks], sp[kt][n]);
          if constexpr (I + kA < NS) rd.template operator()<I + kA>();
          piece.template operator()<I>();
          __builtin_amdgcn_sched_barrier(0);
@@ -434,11 +472,10 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
   };
   auto no_piece = []<int I>() {};
 
-  // Software pipeline, one wave per SIMD: the S products of tile t + 1 are
-  // independent of the softmax and PV products of tile t.  Ring of kAStages
-  // tiles: t (V read by PV), t + 1 (K read by S), t + 2 in flight, t + 3
-  // issued into the buffer tile t - 1 released.
-  constexpr int LPW = T::LPW;
+  // Software pipeline: the S products of tile t + 1 are independent of the
+  // softmax and PV products of tile t.  Ring of kAStages tiles: t (V read by
+  // PV), t + 1 (K read by S), t + 2 in flight, t + 3 issued into the buffer
+  // tile t - 1 released.
   constexpr int ND = DV / 16, kAV = 6;  // PV column tiles; reads (two each) run kAV tiles ahead
   static_assert(ND > kAV && 2 * kAV < 16, "read-ahead must fit the LDS counter");
   int32_t nid[2];  // block ids of the next tile to issue, loaded one iteration ahead
@@ -449,35 +486,37 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
       issue_tile(k, k, nid);
     }
   if (kAStages - 1 < n_tiles) load_ids(kAStages - 1, nid);
-  f32x4 spc[2][2];  // raw scores of the current tile
+  f32x4 spc[2][NQT];  // raw scores of the current tile
   if (n_tiles > 0) {
-    if (n_tiles >= 3) wait_vmcnt<2 * LPW>();
-    else if (n_tiles == 2) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
+    if (n_tiles >= 3) wait_tiles(tiles2{});
+    else if (n_tiles == 2) wait_tiles(tiles1{});
+    else wait_tiles(tiles0{});
     barrier_keep_loads();  // tile 0 visible
     s_tile(lds_addr(stage[0]), spc, no_piece);
   }
   for (int t = 0; t < n_tiles; ++t) {
     // Tile t + 1 resident: at most the loads of tile t + 2 still outstanding.
-    if (t + 2 < n_tiles) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
+    if (t + 2 < n_tiles) wait_tiles(tiles1{});
+    else wait_tiles(tiles0{});
     barrier_keep_loads();  // tile t + 1 visible; every wave is past PV of tile t - 1
     if (t + kAStages - 1 < n_tiles) issue_tile(t + kAStages - 1, (t + kAStages - 1) % kAStages, nid);
 
     // Online softmax of tile t per query (lane column): element e = 4 kt + i
-    // is row 16 kt + 4 g + i of the tile.  Sixteen pieces, one per S step:
-    // for query tile n = I / 8, pieces 0-3 scale and mask two elements each
-    // and keep a running maximum, piece 4 takes the maximum over the four
-    // lane rows and moves the reference (delayed by kSlackP), pieces 5-7 form
-    // the probabilities, their sum and the packed P^T operand.
-    int lim[2];  // element e of query tile n is visible when 16 kt + i <= lim[n]
+    // is row 16 kt + 4 g + i of the tile.  Eight pieces per query tile, run
+    // beside the sixteen S steps (two query tiles: steps 8 n .. 8 n + 7; one:
+    // the even steps): pieces 0-3 scale and mask two elements each and keep
+    // a running maximum, piece 4 takes the maximum over the four lane rows
+    // and moves the reference (delayed by kSlackP), pieces 5-7 form the
+    // probabilities, their sum and the packed P^T operand.
+    int lim[NQT];  // element e of query tile n is visible when 16 kt + i <= lim[n]
 #pragma unroll
-    for (int n = 0; n < 2; ++n) lim[n] = horizon[n] - t * kAT - 4 * g;
-    float sc[2][8], tmx[2], alpha[2], m_use[2], pr[2][8];
-    bf16x8 pB[2];
+    for (int n = 0; n < NQT; ++n) lim[n] = horizon[n] - t * kAT - 4 * g;
+    float sc[NQT][8], tmx[NQT], alpha[NQT], m_use[NQT], pr[NQT][8];
+    bf16x8 pB[NQT];
     auto sm_piece = [&]<int I>() {
-      constexpr int n = I / 8, k = I % 8;
-      if constexpr (k < 4) {
+      constexpr int n = NQT == 2 ? I / 8 : 0, k = NQT == 2 ? I % 8 : I / 2;
+      if constexpr (NQT == 1 && I % 2 == 1) {
+      } else if constexpr (k < 4) {
 #pragma unroll
         for (int e = 2 * k; e < 2 * k + 2; ++e) {
           sc[n][e] = 16 * (e / 4) + (e % 4) <= lim[n] ? spc[e / 4][n][e % 4] * sl2 : -INFINITY;
@@ -508,7 +547,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
 
     // S of tile t + 1 beside the softmax of tile t (on the last tile the S
     // products read a stale buffer that no load targets; they are not used).
-    f32x4 spn[2][2];
+    f32x4 spn[2][NQT];
     s_tile(lds_addr(stage[(t + 1) % kAStages]), spn, sm_piece);
     // The ids of the tile issued next iteration; the next barrier's wait
     // covers their latency.
@@ -522,39 +561,45 @@ __global__ __launch_bounds__(256, 1) void prefill_attend(const PrefillArgs a) {
     };
     [&]<int... I>(std::integer_sequence<int, I...>) { (rdv.template operator()<I>(), ...); }(
         std::make_integer_sequence<int, kAV>{});
-    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {  // rare, uniform
+    bool moved = false;
 #pragma unroll
-      for (int c = 0; c < ND; ++c) {
-        acc[c][0] *= alpha[0];
-        acc[c][1] *= alpha[1];
-      }
+    for (int n = 0; n < NQT; ++n) moved |= alpha[n] != 1.f;
+    if (__ballot(moved)) {  // rare, uniform
+#pragma unroll
+      for (int c = 0; c < ND; ++c)
+#pragma unroll
+        for (int n = 0; n < NQT; ++n) acc[c][n] *= alpha[n];
     }
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (([&] {
          constexpr int issued = I + kAV < ND ? I + kAV : ND;
          lgkm_wait<2 * (issued - 1 - I)>(vv[I][0], vv[I][1]);
          const bf16x8 vA = __builtin_bit_cast(bf16x8, u32x4{vv[I][0].x, vv[I][0].y, vv[I][1].x, vv[I][1].y});
-         acc[I][0] = mfma16x16x32(vA, pB[0], acc[I][0]);
-         acc[I][1] = mfma16x16x32(vA, pB[1], acc[I][1]);
+#pragma unroll
+         for (int n = 0; n < NQT; ++n) acc[I][n] = mfma16x16x32(vA, pB[n], acc[I][n]);
          if constexpr (I + kAV < ND) rdv.template operator()<I + kAV>();
          __builtin_amdgcn_sched_barrier(0);
        }()),
        ...);
     }(std::make_integer_sequence<int, ND>{});
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) spc[kt][0] = spn[kt][0], spc[kt][1] = spn[kt][1];
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int n = 0; n < NQT; ++n) spc[kt][n] = spn[kt][n];
   }
 
   // Block-id errors are seen by the waves that issued the loads: share them.
   if (lane == 0) wflags[w] = flags;
   __syncthreads();
-  flags = wflags[0] | wflags[1] | wflags[2] | wflags[3];
+  flags = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) flags |= wflags[v];
   const bool bad = flags != 0;
   if (tid == 0 && (flags & kBadBlock)) atomicOr(&a.status[b], kBadBlock);
 
   const f32x4 nan4 = {NAN, NAN, NAN, NAN};
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < NQT; ++n) {
     const float l = sum4rows(lsum[n]);
     if (qi[n] >= t_q) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -623,10 +668,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_rope, hipStream_t stream) 
   if (n1 > INT32_MAX || n2 > INT32_MAX) return hipErrorInvalidConfiguration;
   if (d_rope == 64) {
     hipLaunchKernelGGL(prefill_decompress<64>, dim3((unsigned)n1), dim3(256), 0, stream, g);
-    hipLaunchKernelGGL(prefill_attend<64>, dim3((unsigned)n2), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((prefill_attend<64, kAW>), dim3((unsigned)n2), dim3(64 * kAW), 0, stream, g);
   } else {
     hipLaunchKernelGGL(prefill_decompress<0>, dim3((unsigned)n1), dim3(256), 0, stream, g);
-    hipLaunchKernelGGL(prefill_attend<0>, dim3((unsigned)n2), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((prefill_attend<0, kAW>), dim3((unsigned)n2), dim3(64 * kAW), 0, stream, g);
   }
   return hipGetLastError();
 }
