@@ -18,10 +18,12 @@
 //     Tiles of 128 weight rows x 128 cache rows, k-chunks of 64 staged in LDS
 //     by LDS-DMA with an XOR swizzle, 16x16x32 bf16 MFMA with the weights as
 //     the A operand so each lane stores four consecutive output columns.
-//   * prefill_attend: flash attention per (request, head, 128 queries); four
-//     waves of 32 queries each.  Tiles of 32 rows -- K_nope and V from the
-//     workspace, k_pe straight from the paged cache (shared by all heads) --
-//     go HBM -> LDS by LDS-DMA, double-buffered.  S^T = K Q^T with the queries
+//   * prefill_attend: flash attention per (request, head, 128 queries); eight
+//     waves of 16 queries (two per SIMD; a four-wave form of 32 queries per
+//     wave is kept as a template instance).  Tiles of 32 rows -- K_nope and V
+//     from the workspace, k_pe straight from the paged cache (shared by all
+//     heads) -- go HBM -> LDS by LDS-DMA through a four-stage ring, three
+//     tiles in flight.  S^T = K Q^T with the queries
 //     in registers, online softmax with a delayed reference maximum, P^T kept
 //     in registers in the B-operand layout of O^T = V^T P^T, V^T read with the
 //     transposing ds_read_b64_tr_b16.  One barrier per tile: every wave owns
