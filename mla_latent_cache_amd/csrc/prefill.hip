@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a
 // ---------------------------------------------------------------------------
 // Causal flash attention over the decompressed rows
 // ---------------------------------------------------------------------------
-constexpr int kAQ = 128;     // queries per workgroup (128 / NW per wave)
+constexpr int kAQ = 128;     // queries per workgroup (16 per wave)
 constexpr int kAW = 8;       // waves per attention workgroup
 constexpr int kAT = 32;      // cache rows per tile
 constexpr int kAStages = 4;  // tile ring: three tiles in flight while one is used
@@ -221,16 +221,13 @@ struct ATile {
   static constexpr int KP_LOADS = DR > 0 ? 2 * KP_HALF : 0;
   static constexpr int V_LOADS = (kAT * V_P + 63) / 64;
   static constexpr int USED = KN_LOADS + KP_LOADS + V_LOADS;
-  static constexpr int LOADS = (USED + 3) / 4 * 4;            // every wave issues LPW loads
-  static constexpr int LPW = LOADS / 4;
-  static constexpr int STAGE = LOADS * 64;                     // chunks per stage
+  static constexpr int STAGE = USED * 64;                      // chunks per stage
   static constexpr int KP0 = KN_LOADS * 64, V0 = (KN_LOADS + KP_LOADS) * 64;  // region starts (chunks)
   static constexpr int KSTEPS = (DN + DR) / 32, KN_STEPS = DN / 32;
   static_assert(DN % 32 == 0 && DR % 32 == 0, "k-steps of 32 dims");
-  // Region boundaries on multiples of four loads: the j-th load of every
-  // wave lies in one region, known at compile time.
-  static_assert(KN_LOADS % 4 == 0 && KP_LOADS % 4 == 0 && KP_LOADS <= 4, "regions in whole load rounds");
-  static constexpr int region(int j) { return 4 * j < KN_LOADS ? 0 : (4 * j < KN_LOADS + KP_LOADS ? 1 : 2); }
+  // Loads u = w + kAW j: the k_pe loads (fewer than the waves) fall on distinct
+  // waves, so a wave needs the block id of one k_pe block at most.
+  static_assert(KP_LOADS <= kAW, "one k_pe load per wave at most");
   static_assert(16 * (V0 + 16 * V_P) + 32 * (DV / 16) < 65536, "LDS offsets fit the instruction");
 };
 
@@ -257,17 +254,18 @@ __device__ __forceinline__ void lgkm_wait(uint2& x, uint2& y) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N) : "memory");
 }
 
-// NW waves per workgroup: with four, each wave owns 32 queries (two query
-// tiles) and has a SIMD to itself; with eight, 16 queries each and two waves
-// per SIMD, so that one wave's softmax and LDS waits overlap the other's
-// matrix products (the register budget halves to 256).
-template <int DR, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_attend(const PrefillArgs a) {
+// Eight waves per workgroup, 16 queries each, two waves per SIMD: one wave's
+// softmax and LDS waits overlap the other's matrix products (256 registers per
+// wave at most).  (A four-wave form with 32 queries per wave and one wave per
+// SIMD measured the same.)  Query-tile loops run over NQT = 1 tile per wave.
+template <int DR>
+__global__ __launch_bounds__(64 * kAW, 1) void prefill_attend(const PrefillArgs a) {
   using T = ATile<DR>;
   using G = PGeom<DR>;
+  constexpr int NW = kAW;
   constexpr int DN = T::DN, DV = T::DV, D = G::D;
   constexpr int QPW = kAQ / NW, NQT = QPW / 16;  // queries and 16-query tiles per wave
-  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NQT == 1 && kAQ % 16 == 0, "one query tile per wave");
   __shared__ __attribute__((aligned(16))) u32x4 stage[kAStages][T::STAGE];
   __shared__ uint32_t wflags[NW];
 
@@ -319,11 +317,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attend(const PrefillArgs a
   // Tile loads.  Load u of a stage fills chunks [64 u, 64 u + 64): loads
   // [0, KN_LOADS) the K_nope rows (pitch KN_P), then KP_HALF loads per 16-row
   // block of k_pe (pitch KP_P), then the V rows (pitch V_P).  Wave w issues
-  // loads u = w + NW j (with four waves every round is whole, pads included;
-  // with eight, the USED loads only, so wave 0 issues one more than the
-  // others); the lane offsets do not depend on the tile.
-  constexpr int NLD = NW == 4 ? T::LPW : (T::USED + NW - 1) / NW;  // loads of the busiest wave
-  const bool full_w = NW == 4 || w < T::USED - NW * (NLD - 1);     // this wave issues NLD loads
+  // loads u = w + NW j of the USED ones, so the first USED mod NW waves issue
+  // one more than the others; the lane offsets do not depend on the tile.
+  constexpr int NLD = (T::USED + NW - 1) / NW;                  // loads of the busiest wave
+  const bool full_w = w < T::USED - NW * (NLD - 1);             // this wave issues NLD loads
   const uint16_t* kw = a.kw + ((int64_t)b * H + h) * a.max_rows * DN;
   const uint16_t* vw = a.vw + ((int64_t)b * H + h) * a.max_rows * DV;
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
@@ -337,9 +334,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attend(const PrefillArgs a
       const int r = q / T::KN_P, p = q - r * T::KN_P;  // slot p of row r holds chunk p ^ swizzle(r)
       if (r < kAT) v = (uint32_t)(r * DN * 2 + (p ^ row_swizzle<T::KN_CH>(r)) * 16);
     } else if (u < T::KN_LOADS + T::KP_LOADS) {
-      const int ql = q - T::KP0 - ((u - T::KN_LOADS) / T::KP_HALF) * T::KP_HALF * 64;
-      const int r = ql / T::KP_P, p = ql - r * T::KP_P;
-      if (r < 16) v = (uint32_t)(r * D * 2 + (p ^ row_swizzle<T::KP_CH>(r)) * 16);
+      if constexpr (DR > 0) {  // (no k_pe loads without a rope part)
+        const int ql = q - T::KP0 - ((u - T::KN_LOADS) / T::KP_HALF) * T::KP_HALF * 64;
+        const int r = ql / T::KP_P, p = ql - r * T::KP_P;
+        if (r < 16) v = (uint32_t)(r * D * 2 + (p ^ row_swizzle<T::KP_CH>(r)) * 16);
+      }
     } else if (u < T::USED) {
       const int qv = q - T::V0;
       const int r = qv / T::V_P, p = qv - r * T::V_P;
@@ -385,10 +384,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attend(const PrefillArgs a
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int u = w + NW * j;
-      if constexpr (NW == 4) {
-        const i32x4 rs = T::region(j) == 0 ? rs_k : (T::region(j) == 1 ? rs_p : rs_v);
-        dma16(rs, base + 1024u * (uint32_t)u, voffs[j]);
-      } else if (j < NLD - 1 || full_w) {
+      if (j < NLD - 1 || full_w) {
         const i32x4 rs = u < T::KN_LOADS ? rs_k : (u < T::KN_LOADS + T::KP_LOADS ? rs_p : rs_v);
         dma16(rs, base + 1024u * (uint32_t)u, voffs[j]);
       }
@@ -397,12 +393,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_attend(const PrefillArgs a
   // Wait until at most K tiles' loads of this wave are outstanding.
   auto wait_tiles = [&](auto k_tiles) {
     constexpr int K = decltype(k_tiles)::value;
-    if constexpr (NW == 4) {
-      wait_vmcnt<K * NLD>();
-    } else {
-      if (full_w) wait_vmcnt<K * NLD>();
-      else wait_vmcnt<K * (NLD - 1)>();
-    }
+    if (full_w) wait_vmcnt<K * NLD>();
+    else wait_vmcnt<K * (NLD - 1)>();
   };
   using tiles0 = std::integral_constant<int, 0>;
   using tiles1 = std::integral_constant<int, 1>;
@@ -670,10 +662,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int d_rope, hipStream_t stream) 
   if (n1 > INT32_MAX || n2 > INT32_MAX) return hipErrorInvalidConfiguration;
   if (d_rope == 64) {
     hipLaunchKernelGGL(prefill_decompress<64>, dim3((unsigned)n1), dim3(256), 0, stream, g);
-    hipLaunchKernelGGL((prefill_attend<64, kAW>), dim3((unsigned)n2), dim3(64 * kAW), 0, stream, g);
+    hipLaunchKernelGGL(prefill_attend<64>, dim3((unsigned)n2), dim3(64 * kAW), 0, stream, g);
   } else {
     hipLaunchKernelGGL(prefill_decompress<0>, dim3((unsigned)n1), dim3(256), 0, stream, g);
-    hipLaunchKernelGGL((prefill_attend<0, kAW>), dim3((unsigned)n2), dim3(64 * kAW), 0, stream, g);
+    hipLaunchKernelGGL(prefill_attend<0>, dim3((unsigned)n2), dim3(64 * kAW), 0, stream, g);
   }
   return hipGetLastError();
 }
