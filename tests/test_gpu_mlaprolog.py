@@ -71,3 +71,45 @@ def test_prolog_nope_geometry():
 
 def test_prolog_decode_step_full_widths():
     run_case(GLM, 32, hidden=mi.PROLOG_HIDDEN, q_rank=mi.PROLOG_Q_RANK, seed=11)
+
+
+def test_prolog_hip_graph_replay_matches_eager():
+    # The fused prolog captured in one HIP graph and replayed three times, with
+    # eager prolog calls on other inputs between the replays, writes the same
+    # absorbed queries, cache rows and error word as the eager call, bit for bit.
+    spec, n_tok, hidden, q_rank, seed = GLM, 40, 256, 128, 21
+    case = mi.make_case(mi.with_spec(spec, batch=1, seq_len=0, fixed_lens=(16,), max_blocks=1, spare_blocks=0))
+    p = mi.prolog_inputs(spec, n_tok, hidden, q_rank, tag="graph")
+    num_blocks = (n_tok + 15) // 16 + 2
+    slots = mi.random_slots(seed, num_blocks * 16, n_tok, n_skip=2, n_out=0)
+    pos = torch.from_numpy(mi.random_positions(seed + 1, n_tok, 100000)).to(DEV)
+    slots_d = torch.from_numpy(slots).to(DEV)
+    cache0 = to_dev(mi.store(np.random.default_rng(seed).standard_normal((num_blocks, 16, spec.D)), "bf16"))
+    dims = dims_tuple(spec)
+    args = [to_dev(a) for a in (p.x, p.w_dq, p.w_uq, p.w_qr, case.w_uk, p.w_dkv, p.w_kr, p.gamma_q, p.gamma_kv)]
+    ws = torch.empty(mla.mla_prolog_workspace_size(dims, hidden, q_rank, n_tok), dtype=torch.uint8, device=DEV)
+
+    def call(kv, q_abs, err, stream=None):
+        mla.mla_prolog(dims, *args, 1e-6, 1e-6, pos, mi.ROPE_BASE, mla.MLA_ROPE_NEOX, slots_d, kv, q_abs, ws, err,
+                       stream)
+
+    kv_e, q_e = cache0.clone(), torch.empty(n_tok, spec.n_head, spec.D, dtype=torch.bfloat16, device=DEV)
+    err_e = torch.zeros(1, dtype=torch.int32, device=DEV)
+    call(kv_e, q_e, err_e)
+    torch.cuda.synchronize()
+    kv_g, q_g = cache0.clone(), torch.empty_like(q_e)
+    err_g = torch.zeros(1, dtype=torch.int32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        call(kv_g, q_g, err_g, torch.cuda.current_stream())
+    for rep in range(3):
+        kv_g.copy_(cache0)
+        q_g.zero_()
+        err_g.zero_()
+        g.replay()
+        run_case(GLM, 5, hidden=256, q_rank=128, seed=9)  # eager work between replays (synchronises)
+        torch.cuda.synchronize()
+        assert torch.equal(q_g, q_e), rep
+        assert torch.equal(kv_g, kv_e), rep
+        assert torch.equal(err_g, err_e), rep

@@ -134,3 +134,40 @@ def test_prefill_full_size_sampled():
     idx = (sel[:, 0] * s.t_q + sel[:, 1]) * s.n_head + sel[:, 2]
     assert_close(to_host(out).reshape(-1, s.d_v)[idx], ref, "bf16", "full-size prefill out")
     assert_lse_close(to_host(lse).reshape(-1)[idx], ref_lse, "bf16", "full-size prefill lse")
+
+
+def test_prefill_hip_graph_replay_matches_eager():
+    # The call captured in one HIP graph and replayed three times, with eager
+    # calls on other inputs between the replays, reproduces the eager outputs
+    # bit for bit (the call's first kernel clears the status words each time).
+    s = spec("glm52_causal_tq4", name="pf_graph", batch=2, t_q=40, seq_len=0, fixed_lens=(130, 77), max_blocks=10,
+             spare_blocks=2)
+    case = mi.make_case(s)
+    ref_out, ref_lse, status = run_prefill(case)
+    assert status == 0
+    other = mi.make_case(spec("glm52_causal_tq4", name="pf_graph_other", batch=1, t_q=8, seq_len=0, fixed_lens=(50,),
+                              max_blocks=4, spare_blocks=1))
+    dims = dims_tuple(s)
+    B, T, H = s.batch, s.t_q, s.n_head
+    q_nope = to_dev(case.q_nope).view(B, T, H, s.d_nope)
+    q_pe = to_dev(case.q_pe).view(B, T, H, s.d_rope)
+    w_uk, w_uv, kv = to_dev(case.w_uk), to_dev(case.w_uv), to_dev(case.kv)
+    bt, sl = torch.from_numpy(case.block_table).to(DEV), torch.from_numpy(case.seq_lens).to(DEV)
+    out = torch.empty(B, T, H, s.d_v, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=DEV)
+    ws = torch.empty(mla.mla_prefill_workspace_size(dims, B, s.max_blocks), dtype=torch.uint8, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        mla.mla_prefill_attention(dims, case.scale, q_nope, q_pe, w_uk, w_uv, kv, bt, sl, out, lse, ws,
+                                  torch.cuda.current_stream())
+    for rep in range(3):
+        out.zero_()
+        lse.fill_(7.0)
+        g.replay()
+        _, _, other_status = run_prefill(other)  # eager work between replays
+        torch.cuda.synchronize()
+        assert other_status == 0
+        assert mla.mla_decode_status(ws) == 0
+        assert torch.equal(out, ref_out), rep
+        assert torch.equal(lse, ref_lse), rep
