@@ -316,11 +316,19 @@ __global__ __launch_bounds__(64 * kAW, 1) void prefill_attend(const PrefillArgs 
 
   // Tile loads.  Load u of a stage fills chunks [64 u, 64 u + 64): loads
   // [0, KN_LOADS) the K_nope rows (pitch KN_P), then KP_HALF loads per 16-row
-  // block of k_pe (pitch KP_P), then the V rows (pitch V_P).  Wave w issues
-  // loads u = w + NW j of the USED ones, so the first USED mod NW waves issue
-  // one more than the others; the lane offsets do not depend on the tile.
-  constexpr int NLD = (T::USED + NW - 1) / NW;                  // loads of the busiest wave
-  const bool full_w = w < T::USED - NW * (NLD - 1);             // this wave issues NLD loads
+  // block of k_pe (pitch KP_P), then the V rows (pitch V_P).  Each wave loads
+  // from one source, so it builds one buffer resource per tile (the k_pe wave
+  // two, one per block): waves 0-3 take the 16 loads of K_nope and k_pe, four
+  // consecutive each (k_pe, when present, is wave 3's); waves 4-7 take the V
+  // loads u = 16 + (w - 4) + 4 j, wave 4 one more than the others.  The lane
+  // offsets do not depend on the tile.
+  static_assert(T::KN_LOADS + T::KP_LOADS == 16 && T::KN_LOADS % 4 == 0 && (DR == 0 || T::KP_HALF == 2),
+                "four K-side loads per wave of waves 0-3, k_pe (two blocks) on wave 3 only");
+  static_assert(T::V_LOADS > 16 && T::V_LOADS <= 20, "V loads: four per wave of waves 4-7, plus at most four");
+  constexpr int NLD = 5;                                    // loads of the busiest wave
+  const bool kside = w < 4, kpe_w = DR > 0 && w == 3;
+  const int nld_w = kside ? 4 : (w - 4 < T::V_LOADS - 16 ? 5 : 4);  // this wave's loads per tile
+  auto load_u = [&](int j) { return kside ? 4 * w + j : 16 + (w - 4) + 4 * j; };
   const uint16_t* kw = a.kw + ((int64_t)b * H + h) * a.max_rows * DN;
   const uint16_t* vw = a.vw + ((int64_t)b * H + h) * a.max_rows * DV;
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
@@ -328,9 +336,10 @@ __global__ __launch_bounds__(64 * kAW, 1) void prefill_attend(const PrefillArgs 
   uint32_t voffs[NLD];
 #pragma unroll
   for (int j = 0; j < NLD; ++j) {
-    const int u = w + NW * j, q = 64 * u + lane;
+    const int u = load_u(j), q = 64 * u + lane;
     uint32_t v = kOut;
-    if (u < T::KN_LOADS) {
+    if (j >= nld_w) {
+    } else if (u < T::KN_LOADS) {
       const int r = q / T::KN_P, p = q - r * T::KN_P;  // slot p of row r holds chunk p ^ swizzle(r)
       if (r < kAT) v = (uint32_t)(r * DN * 2 + (p ^ row_swizzle<T::KN_CH>(r)) * 16);
     } else if (u < T::KN_LOADS + T::KP_LOADS) {
@@ -363,38 +372,42 @@ __global__ __launch_bounds__(64 * kAW, 1) void prefill_attend(const PrefillArgs 
   auto issue_tile = [&](int t, int buf, const int32_t (&id)[2]) {
     const int j0 = t * kAT;
     const int nval = L - j0 >= kAT ? kAT : (int)(L - j0);  // rows that exist (>= 1)
-    const i32x4 rs_k = raw_rsrc(kw + (int64_t)j0 * DN, (uint32_t)(nval * DN * 2));
-    const i32x4 rs_v = raw_rsrc(vw + (int64_t)j0 * DV, (uint32_t)(nval * DV * 2));
-    i32x4 rs_p = rs_v;
-    if constexpr (DR > 0) {
-      // k_pe of the block of this wave's k_pe load (if it has one: the first
-      // of its loads at or past KN_LOADS); row r of a block at byte r * D * 2
-      // from its column 512.
-      const int up = w + NW * ((T::KN_LOADS - w + NW - 1) / NW);
-      const int hb = up < T::KN_LOADS + T::KP_LOADS ? (up - T::KN_LOADS) / T::KP_HALF : 0;
-      const int nv = nval - 16 * hb <= 0 ? 0 : (nval - 16 * hb >= 16 ? 16 : nval - 16 * hb);
-      const int32_t bid = hb ? id[1] : id[0];
-      const bool ok = (uint32_t)bid < nb32;
-      // every wave checks both blocks, so each wave's flags see every bad id
-      if ((uint32_t)id[0] >= nb32 || (nval > 16 && (uint32_t)id[1] >= nb32)) flags |= kBadBlock;
-      rs_p = raw_rsrc(kv + (int64_t)(ok ? bid : 0) * (16 * D) + G::KR,
-                      ok && nv > 0 ? (uint32_t)((nv - 1) * D * 2 + DR * 2) : 0u);
-    }
     const uint32_t base = lds_addr(stage[buf]);
+    if (kpe_w) {
+      if constexpr (DR > 0) {
+        // k_pe of the tile's two blocks (loads 12, 13: block 0; 14, 15: block
+        // 1); row r of a block at byte r * D * 2 from its column 512.  This
+        // wave checks the ids: the flags of all waves are merged at the end.
+        if ((uint32_t)id[0] >= nb32 || (nval > 16 && (uint32_t)id[1] >= nb32)) flags |= kBadBlock;
+        i32x4 rs[2];
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int u = w + NW * j;
-      if (j < NLD - 1 || full_w) {
-        const i32x4 rs = u < T::KN_LOADS ? rs_k : (u < T::KN_LOADS + T::KP_LOADS ? rs_p : rs_v);
-        dma16(rs, base + 1024u * (uint32_t)u, voffs[j]);
+        for (int hb = 0; hb < 2; ++hb) {
+          const int nv = nval - 16 * hb <= 0 ? 0 : (nval - 16 * hb >= 16 ? 16 : nval - 16 * hb);
+          const int32_t bid = id[hb];
+          const bool ok = (uint32_t)bid < nb32;
+          rs[hb] = raw_rsrc(kv + (int64_t)(ok ? bid : 0) * (16 * D) + G::KR,
+                            ok && nv > 0 ? (uint32_t)((nv - 1) * D * 2 + DR * 2) : 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(rs[j / 2], base + 1024u * (uint32_t)(12 + j), voffs[j]);
       }
+    } else if (kside) {
+      const i32x4 rs_k = raw_rsrc(kw + (int64_t)j0 * DN, (uint32_t)(nval * DN * 2));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(rs_k, base + 1024u * (uint32_t)(4 * w + j), voffs[j]);
+    } else {
+      const i32x4 rs_v = raw_rsrc(vw + (int64_t)j0 * DV, (uint32_t)(nval * DV * 2));
+      const uint32_t vbase = base + 1024u * (uint32_t)(16 + (w - 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16(rs_v, vbase + 4096u * (uint32_t)j, voffs[j]);
+      if (nld_w > 4) dma16(rs_v, vbase + 4096u * 4u, voffs[4]);
     }
   };
   // Wait until at most K tiles' loads of this wave are outstanding.
   auto wait_tiles = [&](auto k_tiles) {
     constexpr int K = decltype(k_tiles)::value;
-    if (full_w) wait_vmcnt<K * NLD>();
-    else wait_vmcnt<K * (NLD - 1)>();
+    if (nld_w > 4) wait_vmcnt<K * 5>();
+    else wait_vmcnt<K * 4>();
   };
   using tiles0 = std::integral_constant<int, 0>;
   using tiles1 = std::integral_constant<int, 1>;
