@@ -1,7 +1,7 @@
 // The fused MLA prolog (CANN operator page "aclnnMlaProlog": the four paths
 // from the hidden states x to the absorbed queries and the cache rows), for
 // gfx950:
-//   c^Q  = RmsNorm(x W^DQ)                  -> gemm 1, finish 1
+//   c^Q  = RmsNorm(x W^DQ)                  -> gemm 1, finish 1 (gain), finish 2 (1 / RMS)
 //   q^C  = c^Q W^UQ,  q^R' = c^Q W^QR        -> gemm 2, finish 2
 //   cache row <- [RmsNorm(x W^DKV) | ROPE(x W^KR)], q^R = ROPE(q^R')
 //                                           -> the cache-append kernel
@@ -115,54 +115,51 @@ __device__ __forceinline__ float sum_splits(const float* p, int64_t sstride, int
 }
 
 // Finish 1, one thread per (token, column): the sums of x W^DQ go to the
-// float32 row the norm reads; those of x W^DKV and x W^KR go to the cache
-// append as they are (bf16).
+// float32 row the norm reads and, times gamma_q, to the bf16 c^Q the second
+// product reads (RmsNorm's per-token 1 / RMS is a scale of the row, so it is
+// applied after that product, in finish 2); those of x W^DKV and x W^KR go to
+// the cache append as they are (bf16).
+constexpr int kFinishPerThread = 16;  // q_rank <= 256 * 16
 __global__ __launch_bounds__(256) void prolog_finish1(const PrologArgs a) {
   const int64_t n = blockIdx.y;
   const int N = a.q_rank + a.kv_rank + a.d_rope;
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= N) return;
   const float v = sum_splits(a.part + n * N + c, a.n_tok * (int64_t)N, a.splits1);
-  if (c < a.q_rank) a.yq[n * a.q_rank + c] = v;
-  else if (c < a.q_rank + a.kv_rank) a.ckv[n * a.kv_rank + (c - a.q_rank)] = f32_to_bf16(v);
-  else a.kpe[n * a.d_rope + (c - a.q_rank - a.kv_rank)] = f32_to_bf16(v);
+  if (c < a.q_rank) {
+    a.yq[n * a.q_rank + c] = v;
+    a.cq[n * a.q_rank + c] = f32_to_bf16(load_gain(a.gamma_q, true, c) * v);
+  } else if (c < a.q_rank + a.kv_rank) {
+    a.ckv[n * a.kv_rank + (c - a.q_rank)] = f32_to_bf16(v);
+  } else {
+    a.kpe[n * a.d_rope + (c - a.q_rank - a.kv_rank)] = f32_to_bf16(v);
+  }
 }
 
-// c^Q = RmsNorm(x W^DQ) per token (gamma_q, eps_q; float32), stored bf16.
-constexpr int kFinishPerThread = 16;  // q_rank <= 256 * 16
-__global__ __launch_bounds__(256) void prolog_norm_q(const PrologArgs a) {
-  const int64_t n = blockIdx.x;
+// Finish 2: the token's 1 / RMS(x W^DQ) (eps_q inside the root; float32, in
+// a fixed order), then the split partials of (gamma c) W^UQ and (gamma c)
+// W^QR summed and scaled by it into q^C [n][H][d_nope] and the unrotated q^R
+// [n][H][d_rope] (bf16).
+__global__ __launch_bounds__(256) void prolog_finish2(const PrologArgs a) {
+  const int64_t n = blockIdx.y;
   const int tid = threadIdx.x;
   const float* y = a.yq + n * a.q_rank;
-  float qv[kFinishPerThread];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < kFinishPerThread; ++j) {
     const int c = tid + 256 * j;
-    qv[j] = c < a.q_rank ? y[c] : 0.f;
-    ss += qv[j] * qv[j];
+    const float v = c < a.q_rank ? y[c] : 0.f;
+    ss += v * v;
   }
   __shared__ float red[4];
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  const float mean = (red[0] + red[1] + red[2] + red[3]) / (float)a.q_rank;
-  const float inv = 1.f / sqrtf(mean + a.eps_q);
-#pragma unroll
-  for (int j = 0; j < kFinishPerThread; ++j) {
-    const int c = tid + 256 * j;
-    if (c < a.q_rank) a.cq[n * a.q_rank + c] = f32_to_bf16(load_gain(a.gamma_q, true, c) * qv[j] * inv);
-  }
-}
-
-// Finish 2: sum the split partials of c^Q W^UQ and c^Q W^QR into q^C
-// [n][H][d_nope] and the unrotated q^R [n][H][d_rope] (bf16).
-__global__ __launch_bounds__(256) void prolog_finish2(const PrologArgs a) {
-  const int64_t n = blockIdx.y;
+  const float inv = 1.f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)a.q_rank + a.eps_q);
   const int NQ = a.n_head * a.d_nope, N = NQ + a.n_head * a.d_rope;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.x * 256 + tid;
   if (c >= N) return;
-  const float v = sum_splits(a.part + n * N + c, a.n_tok * (int64_t)N, a.splits2);
+  const float v = sum_splits(a.part + n * N + c, a.n_tok * (int64_t)N, a.splits2) * inv;
   if (c < NQ) a.qn[n * NQ + c] = f32_to_bf16(v);
   else a.qp[n * (N - NQ) + (c - NQ)] = f32_to_bf16(v);
 }
@@ -243,8 +240,6 @@ hipError_t launch_prolog(const PrologArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prolog_finish1, dim3((unsigned)((g1.N + 255) / 256), (unsigned)a.n_tok), dim3(256), 0, stream,
                      a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(prolog_norm_q, dim3((unsigned)a.n_tok), dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // 2: c^Q [W^UQ; W^QR]^T
   SkinnyGemm g2 = {};
