@@ -85,6 +85,19 @@ def test_small_bf16_every_element(name, num_splits):
     full_compare(case, res, naive_items=0 if spec.q_given else 4)
 
 
+def test_absorb_and_decompress_over_several_token_chunks():
+    # 150 query rows (75 requests x 2 queries): the absorb and decompression
+    # kernels stage tokens 64 at a time, so this runs two full chunks and a
+    # ragged third one (22 rows: one full 16-row tile and 6 more); every element
+    # of q_abs, o_lat and out is compared.
+    lens = tuple(2 + (7 * i) % 40 for i in range(75))
+    spec = spec_small("glm52_many_tokens", "glm52_decode", batch=75, t_q=2, fixed_lens=lens, max_blocks=3)
+    case = mi.make_case(spec)
+    res = run(DeviceCase(case), num_splits=0)
+    assert res["status"] == 0
+    full_compare(case, res, naive_items=4)
+
+
 def test_boundary_lengths_and_empty_requests():
     lens = (0, 1, 15, 16, 17, 31, 32, 33, 0, 63, 64, 65)
     spec = spec_small("glm52_edges", "glm52_decode", batch=len(lens), fixed_lens=lens, max_blocks=6)
