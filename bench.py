@@ -437,8 +437,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build runs the "
-              "decode path on a single MI355X; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the decode path "
+              "runs on a single MI355X; nothing here opens a second device).", file=sys.stderr)
         return 2
 
     import numpy as np
