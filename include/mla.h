@@ -305,7 +305,9 @@ mla_status mla_prolog_workspace_size(const mla_dims* dims, const mla_prolog_dims
  * q_abs [n_tok][n_head][kv_rank + d_rope] type q_dt, data_err as in
  * mla_cache_append (NULL to ignore).  Intermediates (c^Q, the cache
  * inputs, q^C, q^R) are bf16 in the workspace; products and norms
- * accumulate in float32.  Asynchronous on `stream`; the workspace must not
+ * accumulate in float32.  c^Q is stored as gamma_q (x W^DQ), before its
+ * per-token 1 / RMS, which scales the float32 sums of the second product
+ * instead (the products are linear in c^Q; equal up to rounding).  Asynchronous on `stream`; the workspace must not
  * be shared with a concurrent call.
  * Errors: those of mla_prolog_workspace_size, MLA_ERR_UNSUPPORTED (dt not
  * bf16, hidden or q_rank not a multiple of 32, q_rank > 4096, kv_rank,
