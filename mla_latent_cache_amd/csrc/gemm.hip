@@ -15,6 +15,7 @@
 // so its B operand is loaded straight into VGPRs; W_UK is contiguous along the
 // output index, so its slice is staged in LDS and read back with the
 // transposing ds_read_b64_tr_b16.
+#include <type_traits>
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -73,6 +74,18 @@ __device__ __forceinline__ void store_tokens(uint16_t* lds, const bf16x8 (&v)[kS
   }
 }
 
+// Run f with the number of 16-token tiles of a staged chunk (1..4, kTC = 64)
+// as a compile-time constant, so that the tiles' accumulations are
+// independent chains the matrix cores overlap.
+template <typename F>
+__device__ __forceinline__ void dispatch_tiles(int live, F&& f) {
+  static_assert(kTC == 64, "four 16-token tiles per chunk");
+  if (live >= 4) f(std::integral_constant<int, 4>{});
+  else if (live == 3) f(std::integral_constant<int, 3>{});
+  else if (live == 2) f(std::integral_constant<int, 2>{});
+  else if (live == 1) f(std::integral_constant<int, 1>{});
+}
+
 // B operand (tokens as the N dimension) of k-step t for token row `row` of
 // the staged chunk: contraction elements 32 t + 8 g .. + 7.
 __device__ __forceinline__ bf16x8 token_operand(const uint16_t* lds, int row, int K, int t, int g) {
@@ -86,7 +99,10 @@ __device__ __forceinline__ bf16x8 token_operand(const uint16_t* lds, int row, in
 // are the M dimension (read transposed from LDS), tokens the N dimension, so
 // each lane ends with four consecutive columns of one token.
 // ---------------------------------------------------------------------------
-template <typename TO>
+// WIDE (many tokens): the token tiles of a chunk accumulate as independent
+// chains; otherwise one tile after another (faster at decode-step sizes, where
+// a chunk holds one or two tiles).  Both give the same bits.
+template <typename TO, bool WIDE>
 __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_rank, int64_t n_tok,
                                                    const uint16_t* __restrict__ q_nope,
                                                    const uint16_t* __restrict__ q_pe,
@@ -170,13 +186,34 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
       store_tokens(al, v, DN, tid);
       __syncthreads();
     }
-    for (int s16 = 0; s16 < kTC && m0 + s16 < n_tok; s16 += 16) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (WIDE) {
+      const int live = (int)(((n_tok - m0 < kTC ? n_tok - m0 : kTC) + 15) / 16);  // token tiles in the chunk
+      dispatch_tiles(live, [&](auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        f32x4 acc[NT];
 #pragma unroll
-      for (int t = 0; t < kMaxK; ++t)
-        if (t < ksteps) acc = mfma16x16x32(B[t], token_operand(al, s16 + l16, DN, t, g), acc);
-      const int64_t n = m0 + s16 + l16;
-      if (n < n_tok) store4(q_abs, (n * H + h) * D + c0 + cw + 4 * g, acc);
+        for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kMaxK; ++t)
+          if (t < ksteps) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[j] = mfma16x16x32(B[t], token_operand(al, 16 * j + l16, DN, t, g), acc[j]);
+          }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int64_t n = m0 + 16 * j + l16;
+          if (n < n_tok) store4(q_abs, (n * H + h) * D + c0 + cw + 4 * g, acc[j]);
+        }
+      });
+    } else {
+      for (int s16 = 0; s16 < kTC && m0 + s16 < n_tok; s16 += 16) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kMaxK; ++t)
+          if (t < ksteps) acc = mfma16x16x32(B[t], token_operand(al, s16 + l16, DN, t, g), acc);
+        const int64_t n = m0 + s16 + l16;
+        if (n < n_tok) store4(q_abs, (n * H + h) * D + c0 + cw + 4 * g, acc);
+      }
     }
   }
 }
@@ -188,7 +225,7 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int DN, int R, int kv_
 // tokens at a time and read as the N-dimension operand, so each lane ends with
 // output columns j4 .. j4 + 3 of one token.
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO>
+template <typename TI, typename TO, bool WIDE>
 __global__ __launch_bounds__(256) void decompress_mfma(int H, int DV, int KR, int64_t n_tok,
                                                        const TI* __restrict__ o_lat,
                                                        const uint16_t* __restrict__ w_uv,
@@ -214,13 +251,34 @@ __global__ __launch_bounds__(256) void decompress_mfma(int H, int DV, int KR, in
       store_tokens(ol, v, KR, tid);
     }
     __syncthreads();
-    for (int s16 = 0; s16 < kTC && m0 + s16 < n_tok; s16 += 16) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (WIDE) {
+      const int live = (int)(((n_tok - m0 < kTC ? n_tok - m0 : kTC) + 15) / 16);  // token tiles in the chunk
+      dispatch_tiles(live, [&](auto nt_c) {
+        constexpr int NT = decltype(nt_c)::value;
+        f32x4 acc[NT];
 #pragma unroll
-      for (int t = 0; t < kMaxK; ++t)
-        if (t < ksteps) acc = mfma16x16x32(Bk[t], token_operand(ol, s16 + l16, KR, t, g), acc);
-      const int64_t n = m0 + s16 + l16;
-      if (n < n_tok && j4 < DV) store4(out, (n * H + h) * DV + j4, acc);
+        for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kMaxK; ++t)
+          if (t < ksteps) {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[j] = mfma16x16x32(Bk[t], token_operand(ol, 16 * j + l16, KR, t, g), acc[j]);
+          }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int64_t n = m0 + 16 * j + l16;
+          if (n < n_tok && j4 < DV) store4(out, (n * H + h) * DV + j4, acc[j]);
+        }
+      });
+    } else {
+      for (int s16 = 0; s16 < kTC && m0 + s16 < n_tok; s16 += 16) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kMaxK; ++t)
+          if (t < ksteps) acc = mfma16x16x32(Bk[t], token_operand(ol, s16 + l16, KR, t, g), acc);
+        const int64_t n = m0 + s16 + l16;
+        if (n < n_tok && j4 < DV) store4(out, (n * H + h) * DV + j4, acc);
+      }
     }
   }
 }
@@ -283,12 +341,15 @@ hipError_t launch_absorb(int H, int DN, int R, int KR, int64_t n_tok, const void
     const size_t lds = (size_t)DN * 80 * 2 + (size_t)kTC * (DN + 8) * 2;
     const uint16_t *qn = static_cast<const uint16_t*>(q_nope), *qp = static_cast<const uint16_t*>(q_pe),
                    *wk = static_cast<const uint16_t*>(w_uk);
-    if (out_bf16)
-      hipLaunchKernelGGL(absorb_mfma<uint16_t>, grid, dim3(256), lds, stream, H, DN, R, KR, n_tok, qn, qp, wk,
-                         static_cast<uint16_t*>(q_abs));
-    else
-      hipLaunchKernelGGL(absorb_mfma<float>, grid, dim3(256), lds, stream, H, DN, R, KR, n_tok, qn, qp, wk,
-                         static_cast<float*>(q_abs));
+    // Independent tile chains from two chunks on (measured: slower for one chunk).
+    const bool wide = n_tok > kTC;
+    if (out_bf16) {
+      auto k = wide ? absorb_mfma<uint16_t, true> : absorb_mfma<uint16_t, false>;
+      hipLaunchKernelGGL(k, grid, dim3(256), lds, stream, H, DN, R, KR, n_tok, qn, qp, wk, static_cast<uint16_t*>(q_abs));
+    } else {
+      auto k = wide ? absorb_mfma<float, true> : absorb_mfma<float, false>;
+      hipLaunchKernelGGL(k, grid, dim3(256), lds, stream, H, DN, R, KR, n_tok, qn, qp, wk, static_cast<float*>(q_abs));
+    }
     return hipGetLastError();
   }
   const unsigned grid = generic_grid(n_tok * H * (KR + R));
@@ -322,9 +383,11 @@ hipError_t launch_decompress(int H, int DV, int KR, int64_t n_tok, const void* o
     const dim3 grid(H, (DV + kCols - 1) / kCols);
     const uint16_t* wv = static_cast<const uint16_t*>(w_uv);
     const size_t lds = (size_t)kTC * (KR + 8) * 2;
-#define MLA_DECOMP(TI, TO)                                                                               \
-  hipLaunchKernelGGL((decompress_mfma<TI, TO>), grid, dim3(256), lds, stream, H, DV, KR, n_tok,            \
-                     static_cast<const TI*>(o_lat), wv, static_cast<TO*>(out))
+    // Independent tile chains from 33 tokens on (measured: slower at 32).
+    const bool wide = n_tok > 32;
+#define MLA_DECOMP(TI, TO)                                                                                 \
+  hipLaunchKernelGGL((wide ? decompress_mfma<TI, TO, true> : decompress_mfma<TI, TO, false>), grid, dim3(256), \
+                     lds, stream, H, DV, KR, n_tok, static_cast<const TI*>(o_lat), wv, static_cast<TO*>(out))
     if (o_bf16 && out_bf16) MLA_DECOMP(uint16_t, uint16_t);
     else if (o_bf16) MLA_DECOMP(uint16_t, float);
     else if (out_bf16) MLA_DECOMP(float, uint16_t);
