@@ -13,7 +13,7 @@ import torch
 import mla_inputs as mi
 import mla_latent_cache_amd as mla
 import oracle
-from gpu_util import (DeviceCase, assert_close, assert_lse_close, dims_tuple, flat_index, oracle_dims,
+from gpu_util import (DEV, DeviceCase, assert_close, assert_lse_close, dims_tuple, flat_index, oracle_dims,
                       oracle_q_abs, paged, run, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
@@ -96,6 +96,33 @@ def test_absorb_and_decompress_over_several_token_chunks():
     res = run(DeviceCase(case), num_splits=0)
     assert res["status"] == 0
     full_compare(case, res, naive_items=4)
+
+
+def test_many_token_instances_give_the_same_bits():
+    # Above one 64-token chunk (absorb) or 32 tokens (decompression) the
+    # kernels run the chunk's token tiles as independent accumulator chains;
+    # every output is still the same sequence of products, so the leading
+    # tokens of a wider call must match the narrower call bit for bit.
+    torch.manual_seed(11)
+    H, DN, R, DV, KR = 64, 192, 64, 256, 512
+    dims = (H, DN, R, DV, KR)
+    wuk = (torch.randn(H, DN, KR) * 0.05).bfloat16().to(DEV)
+    wuv = (torch.randn(H, DV, KR) * 0.05).bfloat16().to(DEV)
+    qn = torch.randn(150, H, DN).bfloat16().to(DEV)
+    qp = torch.randn(150, H, R).bfloat16().to(DEV)
+    ol = torch.randn(150, H, KR).bfloat16().to(DEV)
+    for narrow_a, narrow_d in ((64, 32), (5, 17)):
+        qa_w = torch.empty(150, H, KR + R, dtype=torch.bfloat16, device=DEV)
+        qa_n = torch.empty(narrow_a, H, KR + R, dtype=torch.bfloat16, device=DEV)
+        mla.mla_absorb_q(dims, qn, qp, wuk, qa_w)
+        mla.mla_absorb_q(dims, qn[:narrow_a].contiguous(), qp[:narrow_a].contiguous(), wuk, qa_n)
+        out_w = torch.empty(150, H, DV, dtype=torch.bfloat16, device=DEV)
+        out_n = torch.empty(narrow_d, H, DV, dtype=torch.bfloat16, device=DEV)
+        mla.mla_decompress_v(dims, ol, wuv, out_w)
+        mla.mla_decompress_v(dims, ol[:narrow_d].contiguous(), wuv, out_n)
+        torch.cuda.synchronize()
+        assert torch.equal(qa_w[:narrow_a], qa_n)
+        assert torch.equal(out_w[:narrow_d], out_n)
 
 
 def test_boundary_lengths_and_empty_requests():
