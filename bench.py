@@ -3,17 +3,21 @@
 One step = one pass of the whole hot path over one batch of synthetic input,
 with every input already resident in HBM:
     mla_absorb_q -> mla_decode_attention (split-KV kernel + LSE merge) -> mla_decompress_v
-Default workload: GLM-5.2 geometry decode (64 heads, d_nope 192, d_rope 64,
-d_v 256, kv_rank 512; 32 requests x 4096 cached rows; 16-row blocks; bf16).
+(the decode call alone where the absorbed queries are given).
+Default workload: DeepSeek-V3-shaped ragged decode (128 heads, 576-wide
+absorbed queries given directly, kv_rank 512 + rope 64; 64 requests with
+lengths uniform in [0, 32768], requests 0 and 63 empty; 16-row blocks; bf16).
+The GLM-5.2, causal t_q = 4 and NoPE workloads are timed the same way and
+reported under "workloads".
 
 Consecutive steps cycle through --copies independent copies of every input
 (cache, block table, queries, weights), so the 256 MB Infinity Cache cannot
 serve a step from the previous one.  The timed region replays one HIP graph
-per input copy holding the step's four kernels (--eager launches them from
-the host instead); the decode call's own duration for the roofline comes
-from HIP events on its stream around each call.  The CPU baseline runs the oracle
-(absorbed form: absorb, two-pass attention, decompress) over the same
-workload on the host cores.
+per input copy holding the step's kernels (--eager launches them from the
+host instead); the decode call's own duration for the roofline comes from
+HIP events on its stream around each call.  The CPU baseline runs the oracle
+over the same workload on the host cores (and on one thread for the tiny
+workload and a GLM-5.2 sample).
 
 Prints one JSON line.  Throughput `value` is algorithmic decode-path bytes
 per second (GB/s): KV rows read once, queries, weights, outputs, block table
@@ -37,10 +41,11 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
 # Measured HBM traffic of one decode call (FETCH_SIZE and WRITE_SIZE counter
-# runs, calibrated against a device copy of known size) lives in a profile
-# summary, tagged with a hash of the sources it was measured on; it is reported
-# only while those sources are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_glm52_hbm_traffic.md")
+# runs, calibrated against a device copy of known size) lives in profile
+# summaries (profiles/decode_*_hbm_traffic.md), each tagged with its workload
+# and a hash of the sources it was measured on; a figure is reported only
+# while those sources are unchanged.
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["mla_latent_cache_amd/csrc/decode.hip", "mla_latent_cache_amd/csrc/device_common.hpp",
                   "mla_latent_cache_amd/csrc/kernels.hpp", "mla_latent_cache_amd/csrc/mla_api.cpp"]
 
@@ -55,20 +60,19 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """Bytes per decode call from the committed counter summary, or None when
+    """Bytes per decode call from a committed counter summary, or None when
     there is none for this workload or the kernel sources changed since."""
+    import glob
     import re
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    m = re.search(r"<!-- traffic: (\{.*?\}) -->", text, re.S)
-    if not m:
-        return None
-    rec = json.loads(m.group(1))
-    if rec.get("workload") != workload or rec.get("source_sha256") != kernel_source_hash():
-        return None
-    return int(rec["bytes_per_call"])
+    for path in sorted(glob.glob(os.path.join(PROFILES, "decode_*_hbm_traffic.md"))):
+        text = open(path).read()
+        m = re.search(r"<!-- traffic: (\{.*?\}) -->", text, re.S)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("workload") == workload and rec.get("source_sha256") == kernel_source_hash():
+            return int(rec["bytes_per_call"])
+    return None
 
 
 def log(msg: str) -> None:
@@ -133,7 +137,8 @@ def cpu_baseline(spec, case, figs, max_items: int):
         "cores": oracle.threads(),
         "kind": "oracle",
         "sample": ("whole workload" if sel is None else f"{n} of {n_all} (request, query, head) items, seeded")
-                  + f", absorbed form in float64, {dt:.2f} s wall",
+                  + (", paged decode of the given absorbed queries" if spec.q_given else ", absorbed form")
+                  + f" in float64, {dt:.2f} s wall",
         "tokens_heads_per_s": round(figs["tokens_heads"] * frac / dt, 1),
         "seconds": round(dt, 3),
     }
@@ -416,15 +421,188 @@ def time_prefill(name: str = "glm52_prefill", reps: int = 10):
     }
 
 
+def decode_figures_only(figs):
+    return {k: figs[k] for k in ("decode_bytes", "decode_flops", "kv_bytes", "tokens_heads")}
+
+
+def measure(name: str, steps: int, warmup: int, n_copies: int, num_splits: int, eager: bool, with_ev: bool = True):
+    """Time one workload: the whole step (absorb -> decode -> decompress, or
+    the decode call alone when the absorbed queries are given) replayed from
+    HIP graphs over `n_copies` input copies, and the decode call alone with
+    HIP events on its stream.  Returns (record, case, copies, stream)."""
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_latent_cache_amd as mla
+
+    spec = mi.SPECS[name]
+    log(f"workload {spec.name}: generating inputs")
+    case = mi.make_case(spec)
+    figs = work_figures(spec, case.seq_lens)
+    dims = (spec.n_head, spec.d_nope, spec.d_rope, spec.d_v, spec.kv_rank)
+    B, T, H, D, R = spec.batch, spec.t_q, spec.n_head, spec.D, spec.kv_rank
+    sdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    copies = []
+    for k in range(max(1, n_copies)):
+        c = {"kv": dev(case.kv), "bt": torch.from_numpy(case.block_table).cuda(),
+             "sl": torch.from_numpy(case.seq_lens).cuda()}
+        if spec.q_given:
+            c["q_abs"] = dev(case.q_abs)
+        else:
+            c.update(q_nope=dev(case.q_nope), q_pe=dev(case.q_pe) if spec.d_rope else None,
+                     w_uk=dev(case.w_uk), w_uv=dev(case.w_uv),
+                     q_abs=torch.empty(B, T, H, D, dtype=sdt, device="cuda"))
+        c["out_lat"] = torch.empty(B, T, H, R, dtype=sdt, device="cuda")
+        c["lse"] = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
+        if not spec.q_given:
+            c["out"] = torch.empty(B * T, H, spec.d_v, dtype=sdt, device="cuda")
+        copies.append(c)
+    splits = mla.mla_decode_resolve_splits(dims, B, T, spec.max_blocks, num_splits)
+    ws = torch.empty(mla.mla_decode_workspace_size(dims, B, T, spec.max_blocks, 16, num_splits),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(c, ev=None):
+        stream = torch.cuda.current_stream()
+        if not spec.q_given:
+            mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.mla_decode_attention(dims, case.scale, c["q_abs"], c["kv"], c["bt"], c["sl"], c["out_lat"], c["lse"],
+                                 ws, num_splits, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if not spec.q_given:
+            mla.mla_decompress_v(dims, c["out_lat"], c["w_uv"], c["out"], stream)
+
+    log(f"{spec.name}: warmup {warmup} steps ({splits} ranges per query tile, {len(copies)} input copies)")
+    for k in range(warmup):
+        step(copies[k % len(copies)])
+    torch.cuda.synchronize()
+    status = mla.mla_decode_status(ws)
+    if status:
+        raise RuntimeError(f"{spec.name}: device data-error flags {status:#x}")
+
+    # The step's kernels are captured in one HIP graph per input copy, as a
+    # serving loop would launch them; the timed region replays them.  With
+    # eager, every kernel is launched from the host.
+    stream = torch.cuda.current_stream()
+    graphs = []
+    if not eager:
+        cap = torch.cuda.Stream()
+        for c in copies:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(c)
+            graphs.append(g)
+        for k in range(max(1, warmup)):
+            graphs[k % len(graphs)].replay()
+        torch.cuda.synchronize()
+
+    # Timed region: the whole step, K times.
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(steps):
+        if graphs:
+            graphs[k % len(graphs)].replay()
+        else:
+            step(copies[k % len(copies)])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+
+    # The decode call alone: HIP events on its stream around each call.
+    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(steps):
+        step(copies[k % len(copies)], ev_dec[k])
+    torch.cuda.synchronize()
+    dec_ms = sorted(a.elapsed_time(b) for a, b in ev_dec)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    log(f"{spec.name}: {ms_step * 1e3:.1f} us/step ({'host launches' if eager else 'HIP graph replay'}); "
+        f"decode call avg {dec_avg * 1e3:.1f} us (min {dec_ms[0] * 1e3:.1f})")
+
+    stage = {}
+    if not spec.q_given:
+        for nm in ("absorb", "decompress"):
+            es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for k, (a, b) in enumerate(es):
+                c = copies[k % len(copies)]
+                a.record(stream)
+                if nm == "absorb":
+                    mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
+                else:
+                    mla.mla_decompress_v(dims, c["out_lat"], c["w_uv"], c["out"], stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            stage[nm] = sum(a.elapsed_time(b) for a, b in es) / len(es)
+    stage["decode"] = dec_avg
+
+    dec_s = dec_avg * 1e-3
+    dec_gbs = figs["decode_bytes"] / dec_s / 1e9
+    dec_tflops = figs["decode_flops"] / dec_s / 1e12
+    rec = {
+        "workload": f"{spec.name}: {H} heads, d_nope {spec.d_nope}, d_rope {spec.d_rope}, d_v {spec.d_v}, "
+                    f"kv_rank {R}, batch {B} x t_q {T}, cache rows per request "
+                    f"{'ragged' if spec.lengths == 'ragged' else int(case.seq_lens[0])}, block 16",
+        "batch": B, "t_q": T, "seq_lens_total": int(np.maximum(case.seq_lens, 0).sum()),
+        "ranges_per_query_tile": splits, "input_copies": len(copies),
+        "step_us": round(ms_step * 1e3, 2),
+        "step_launch": "host launches" if eager else "HIP graph replay",
+        "step_bytes": figs["bytes"], "step_gbs": round(figs["bytes"] / (ms_step * 1e-3) / 1e9, 2),
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "decode_us": round(dec_avg * 1e3, 2), "decode_min_us": round(dec_ms[0] * 1e3, 2),
+        "decode_bytes": figs["decode_bytes"], "decode_flops": figs["decode_flops"],
+        "decode_gbs": round(dec_gbs, 2), "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_tflops": round(dec_tflops, 2), "decode_mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
+        "bound": "mfma" if figs["decode_flops"] / figs["decode_bytes"] > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
+                 else "hbm",
+        "tokens_heads_per_s": round(figs["tokens_heads"] / (ms_step * 1e-3), 1),
+    }
+    rec["decode_roofline_frac"] = rec["decode_mfma_frac"] if rec["bound"] == "mfma" else rec["decode_hbm_frac"]
+    return rec, figs, case, copies, stream
+
+
+def single_thread_oracle():
+    """The oracle on one host thread: the tiny f32 workload in full, and a
+    seeded sample of 256 (request, query, head) items of the GLM-5.2 decode
+    workload (absorbed form), each scaled to GB/s of its workload's
+    algorithmic bytes."""
+    import mla_inputs as mi
+    import oracle
+
+    out = {}
+    prev = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        for name, items in (("tiny_f32", None), ("glm52_decode", 256)):
+            spec = mi.SPECS[name]
+            case = mi.make_case(spec)
+            figs = work_figures(spec, case.seq_lens)
+            rec = cpu_baseline(spec, case, figs, items if items is not None else 1 << 30)
+            out[name] = {k: rec[k] for k in ("value", "unit", "cores", "sample", "tokens_heads_per_s", "seconds")}
+    finally:
+        oracle.set_threads(prev)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="glm52_decode")
+    ap.add_argument("--workload", default="dsv3_ragged")
+    ap.add_argument("--extra-workloads", default="glm52_decode,glm52_causal_tq4,nope_long,nope_wide",
+                    help="comma-separated workloads also timed and reported under 'workloads' ('' for none)")
     ap.add_argument("--copies", type=int, default=4, help="input copies cycled across steps")
     ap.add_argument("--num-splits", type=int, default=0, help="KV splits per request (0 = automatic)")
-    ap.add_argument("--cpu-items", type=int, default=4096, help="oracle items for the CPU baseline")
+    ap.add_argument("--cpu-items", type=int, default=8192, help="oracle items for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the naive-form prefill measurement")
     ap.add_argument("--no-dcp", action="store_true", help="skip the context-parallel share measurement")
@@ -441,7 +619,6 @@ def main() -> int:
               "runs on a single MI355X; nothing here opens a second device).", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import mla_inputs as mi
@@ -452,124 +629,30 @@ def main() -> int:
         return 2
     mla.lib()  # fails loudly when the HIP library is missing
     torch.cuda.set_device(0)
+
+    main_rec, figs, case, copies, stream = measure(args.workload, args.steps, args.warmup, args.copies,
+                                                   args.num_splits, args.eager)
     spec = mi.SPECS[args.workload]
-    log(f"workload {spec.name}: generating inputs")
-    case = mi.make_case(spec)
-    figs = work_figures(spec, case.seq_lens)
     dims = (spec.n_head, spec.d_nope, spec.d_rope, spec.d_v, spec.kv_rank)
-    B, T, H, D, R = spec.batch, spec.t_q, spec.n_head, spec.D, spec.kv_rank
-    sdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
 
-    def dev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
-
-    copies = []
-    for k in range(max(1, args.copies)):
-        c = {"kv": dev(case.kv), "bt": torch.from_numpy(case.block_table).cuda(),
-             "sl": torch.from_numpy(case.seq_lens).cuda()}
-        if spec.q_given:
-            c["q_abs"] = dev(case.q_abs)
-        else:
-            c.update(q_nope=dev(case.q_nope), q_pe=dev(case.q_pe) if spec.d_rope else None,
-                     w_uk=dev(case.w_uk), w_uv=dev(case.w_uv),
-                     q_abs=torch.empty(B, T, H, D, dtype=sdt, device="cuda"))
-        c["out_lat"] = torch.empty(B, T, H, R, dtype=sdt, device="cuda")
-        c["lse"] = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
-        if not spec.q_given:
-            c["out"] = torch.empty(B * T, H, spec.d_v, dtype=sdt, device="cuda")
-        copies.append(c)
-    splits = mla.mla_decode_resolve_splits(dims, B, T, spec.max_blocks, args.num_splits)
-    ws = torch.empty(mla.mla_decode_workspace_size(dims, B, T, spec.max_blocks, 16, args.num_splits),
-                     dtype=torch.uint8, device="cuda")
-    def step(c, ev=None):
-        stream = torch.cuda.current_stream()
-        if not spec.q_given:
-            mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
-        if ev is not None:
-            ev[0].record(stream)
-        mla.mla_decode_attention(dims, case.scale, c["q_abs"], c["kv"], c["bt"], c["sl"], c["out_lat"], c["lse"],
-                                 ws, args.num_splits, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        if not spec.q_given:
-            mla.mla_decompress_v(dims, c["out_lat"], c["w_uv"], c["out"], stream)
-
-    log(f"warmup {args.warmup} steps ({splits} splits per request, {len(copies)} input copies)")
-    for k in range(args.warmup):
-        step(copies[k % len(copies)])
-    torch.cuda.synchronize()
-    status = mla.mla_decode_status(ws)
-    if status:
-        log(f"device data-error flags {status:#x}")
-        return 1
-
-    # The step's four kernels (absorb, split, merge, decompress) are captured in
-    # one HIP graph per input copy, as a serving loop would launch them; the
-    # timed region replays them.  --eager launches every kernel from the host.
-    stream = torch.cuda.current_stream()
-    graphs = []
-    if not args.eager:
-        cap = torch.cuda.Stream()
-        for c in copies:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                step(c)
-            graphs.append(g)
-        for k in range(max(1, args.warmup)):
-            graphs[k % len(graphs)].replay()
-        torch.cuda.synchronize()
-
-    # Timed region: the whole step.
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for k in range(args.steps):
-        if graphs:
-            graphs[k % len(graphs)].replay()
-        else:
-            step(copies[k % len(copies)])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-
-    # The decode call alone: HIP events on its stream around each call.
-    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    for k in range(args.steps):
-        step(copies[k % len(copies)], ev_dec[k])
-    torch.cuda.synchronize()
-    dec_ms = sorted(a.elapsed_time(b) for a, b in ev_dec)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    log(f"{ms_step * 1e3:.1f} us/step ({'host launches' if args.eager else 'HIP graph replay'}); "
-        f"decode call avg {dec_avg * 1e3:.1f} us (min {dec_ms[0] * 1e3:.1f})")
-
-    # Stage split (separate, untimed-for-value pass): absorb and decompress alone.
-    stage = {}
-    if not spec.q_given:
-        for name in ("absorb", "decompress"):
-            es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-            for k, (a, b) in enumerate(es):
-                c = copies[k % len(copies)]
-                a.record(stream)
-                if name == "absorb":
-                    mla.mla_absorb_q(dims, c["q_nope"], c["q_pe"], c["w_uk"], c["q_abs"], stream)
-                else:
-                    mla.mla_decompress_v(dims, c["out_lat"], c["w_uv"], c["out"], stream)
-                b.record(stream)
-            torch.cuda.synchronize()
-            stage[name] = sum(a.elapsed_time(b) for a, b in es) / len(es)
-    stage["decode"] = dec_avg
-
-    prolog = time_prolog(spec, case, dims, copies[0]["kv"], stream)
-    stage["cache_append"] = prolog["decode_step_us"] * 1e-3
+    # Other workloads: each timed the same way (fewer input copies), reported as records.
+    extras = {}
+    extra_names = [w for w in args.extra_workloads.split(",") if w and w != args.workload]
+    sub = {}
+    for w in extra_names:
+        rec, f2, c2, cp2, _ = measure(w, args.steps, args.warmup, min(args.copies, 2), args.num_splits, args.eager)
+        extras[w] = rec
+        s2 = mi.SPECS[w]
+        if w == "glm52_decode":
+            d2 = (s2.n_head, s2.d_nope, s2.d_rope, s2.d_v, s2.kv_rank)
+            sub["prolog"] = time_prolog(s2, c2, d2, cp2[0]["kv"], stream)
+            if not args.no_dcp:
+                sub["dcp"] = time_dcp(s2, c2, d2, cp2[0]["q_abs"], stream)
+            if not args.no_mlaprolog:
+                sub["mlaprolog"] = time_mlaprolog(s2, c2, d2)
+        del cp2
+        torch.cuda.empty_cache()
     prefill = None if args.no_prefill else time_prefill()
-    dcp = time_dcp(spec, case, dims, copies[0]["q_abs"], stream) if (spec.name == "glm52_decode" and not args.no_dcp) \
-        else None
-    mlaprolog = time_mlaprolog(spec, case, dims) if (not spec.q_given and spec.dtype == "bf16"
-                                                     and not args.no_mlaprolog) else None
 
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -580,9 +663,9 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.copy_calibration_mb} MiB device-to-device")
 
+    ms_step = main_rec["step_us"] * 1e-3
     value = figs["bytes"] / (ms_step * 1e-3) / 1e9
-    dec_gbs = figs["decode_bytes"] / (dec_avg * 1e-3) / 1e9
-    dec_tflops = figs["decode_flops"] / (dec_avg * 1e-3) / 1e12
+    bound = main_rec["bound"]
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -596,38 +679,37 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": spec.dtype,
         "data": "synthetic (seeded SplitMix64 normals; RMS-normalised latent rows; shuffled block tables)",
-        "config": {
-            "workload": f"{spec.name}: {H} heads, d_nope {spec.d_nope}, d_rope {spec.d_rope}, d_v {spec.d_v}, "
-                        f"kv_rank {R}, batch {B} x t_q {T}, cache rows per request "
-                        f"{'ragged' if spec.lengths == 'ragged' else int(case.seq_lens[0])}, block 16",
-            "batch": B, "t_q": T, "seq_lens_total": int(np.maximum(case.seq_lens, 0).sum()),
-            "splits_per_request": splits, "input_copies": len(copies),
-        },
+        "config": {k: main_rec[k] for k in ("workload", "batch", "t_q", "seq_lens_total", "ranges_per_query_tile",
+                                            "input_copies")},
         "tflops": round(figs["flops"] / (ms_step * 1e-3) / 1e12, 3),
-        "tokens_heads_per_s": round(figs["tokens_heads"] / (ms_step * 1e-3), 1),
-        "step_launch": "host launches" if args.eager else "HIP graph replay (absorb, split, merge, decompress)",
-        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
-        "prolog": prolog,
-        "prefill": prefill,
-        "dcp": dcp,
-        "mlaprolog": mlaprolog,
+        "tokens_heads_per_s": main_rec["tokens_heads_per_s"],
+        "step_launch": main_rec["step_launch"],
+        "stages_us": main_rec["stages_us"],
         "roofline": {
-            "kernel": "decode call: decode_split_mfma + decode_merge",
-            "bound": "hbm",
-            "achieved": round(dec_gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "kernel": "decode call (one C-ABI call: split-KV kernel + LSE merge)",
+            "bound": bound,
+            "achieved": main_rec["decode_gbs"] if bound == "hbm" else main_rec["decode_tflops"],
+            "peak": HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS,
+            "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+            "frac": main_rec["decode_roofline_frac"],
             "traffic": measured_traffic(spec.name),
             "algorithmic_bytes_per_launch": figs["decode_bytes"],
-            "avg_launch_us": round(dec_avg * 1e3, 2),
-            "mfma_tflops": round(dec_tflops, 2),
-            "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": figs["decode_flops"],
+            "avg_launch_us": main_rec["decode_us"],
+            "hbm_frac": main_rec["decode_hbm_frac"],
+            "mfma_tflops": main_rec["decode_tflops"],
+            "mfma_frac": main_rec["decode_mfma_frac"],
         },
+        "workloads": extras,
+        "prefill": prefill,
     }
+    result.update(sub)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")
-        result["cpu_baseline"] = cpu_baseline(spec, case, figs, args.cpu_items)
+        cb = cpu_baseline(spec, case, figs, args.cpu_items)
+        log("cpu baseline: oracle on one host thread (tiny and GLM-5.2 sample)")
+        cb["single_thread"] = single_thread_oracle()
+        result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
     return 0
 

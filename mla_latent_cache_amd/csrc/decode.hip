@@ -1029,8 +1029,13 @@ Plan decode_plan(int n_head, int kv_rank, int d_rope, int batch, int t_q, int ma
   p.chunk_blocks = (max_blocks + p.splits - 1) / p.splits;
   p.splits = (max_blocks + p.chunk_blocks - 1) / p.chunk_blocks;  // no empty tail ranges
   p.m_tiles = p.mfma ? (n_q + kQRowsPerWG - 1) / kQRowsPerWG : n_q;
-  p.n_pairs = batch * p.splits;
-  p.n_items = p.n_pairs * p.m_tiles;
+  // Workgroup and status-slot counts are 32-bit on the device (and the grid
+  // rounds the pairs up to a multiple of 8): larger plans are refused.
+  const int64_t pairs = (int64_t)batch * p.splits;
+  const int64_t rounded = (pairs + 7) / 8 * 8;
+  p.ok = p.m_tiles >= 1 && rounded <= (int64_t)INT32_MAX / p.m_tiles;
+  p.n_pairs = p.ok ? (int)pairs : 0;
+  p.n_items = p.ok ? (int)(pairs * p.m_tiles) : 0;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t status_bytes = al((size_t)(p.n_items > 0 ? p.n_items : 1) * 4);
   p.lse_off = kHeaderBytes + status_bytes;

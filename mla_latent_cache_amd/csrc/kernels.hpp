@@ -46,6 +46,7 @@ struct DecodeArgs {
 struct Plan {
   int splits, chunk_blocks, m_tiles, n_pairs, n_items;
   bool mfma;
+  bool ok;  // counts fit the device's 32-bit indices
   size_t lse_off, o_off, bytes;
 };
 

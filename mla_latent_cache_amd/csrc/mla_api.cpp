@@ -14,6 +14,11 @@ namespace {
 
 bool dt_ok(mla_dtype d) { return d == MLA_F32 || d == MLA_BF16; }
 
+// The kernels read and write tensors in 16-byte vectors (and stage cache
+// blocks with 16-byte buffer loads), index arrays and LSE as 4-byte words, and
+// lay the workspace out in 256-byte sections.
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
 // Compute units of the current device (cached per device id).
 int device_cus(int* out) {
   static int cache[64] = {0};
@@ -106,6 +111,8 @@ mla_status mla_absorb_q(const mla_dims* dims, int64_t n_tok, const void* q_nope,
   if (!dt_ok(in_dt) || !dt_ok(out_dt)) return MLA_ERR_ARG;
   if (n_tok == 0) return MLA_OK;
   if (!q_nope || !w_uk || !q_abs || (dims->d_rope > 0 && !q_pe)) return MLA_ERR_NULL;
+  if (!aligned(q_nope, 16) || !aligned(w_uk, 16) || !aligned(q_abs, 16) || (q_pe && !aligned(q_pe, 16)))
+    return MLA_ERR_ARG;
   const hipError_t e = mla::launch_absorb(dims->n_head, dims->d_nope, dims->d_rope, dims->kv_rank, n_tok, q_nope,
                                           q_pe, w_uk, in_dt == MLA_BF16, q_abs, out_dt == MLA_BF16,
                                           static_cast<hipStream_t>(stream));
@@ -137,6 +144,7 @@ mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_
                                         true);
   const mla::Plan p2 = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
                                         false);
+  if (!p1.ok || !p2.ok) return MLA_ERR_SHAPE;
   *bytes = p1.bytes > p2.bytes ? p1.bytes : p2.bytes;
   return MLA_OK;
 }
@@ -155,6 +163,9 @@ static mla_status decode_impl(const mla_dims* dims, float scale, int32_t batch, 
   if (!(scale > 0.f) || !isfinite(scale)) return MLA_ERR_ARG;
   if (!workspace) return MLA_ERR_NULL;
   if (batch > 0 && (!q_abs || !kv_cache || !block_table || !seq_lens || !out_lat)) return MLA_ERR_NULL;
+  if (!aligned(q_abs, 16) || !aligned(kv_cache, 16) || !aligned(out_lat, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(lse, 4) || !aligned(workspace, 256))
+    return MLA_ERR_ARG;
   const bool bf16 = dt == MLA_BF16;
   const bool mfma = mfma_path(dims, bf16);
   if (!mfma && dims->kv_rank > 1024) return MLA_ERR_UNSUPPORTED;
@@ -164,6 +175,7 @@ static mla_status decode_impl(const mla_dims* dims, float scale, int32_t batch, 
   const mla_status r = resolve(dims, batch, t_q, max_blocks, num_splits, bf16, &splits);
   if (r != MLA_OK) return r;
   const mla::Plan p = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits, bf16);
+  if (!p.ok) return MLA_ERR_SHAPE;
   size_t need = 0;
   const mla_status ws = mla_decode_workspace_size(dims, batch, t_q, max_blocks, block_size, splits, &need);
   if (ws != MLA_OK) return ws;
@@ -246,6 +258,7 @@ mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_l
   if (!dt_ok(o_dt) || !dt_ok(w_dt) || !dt_ok(out_dt)) return MLA_ERR_ARG;
   if (n_tok == 0) return MLA_OK;
   if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned(o_lat, 16) || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_ARG;
   const hipError_t e = mla::launch_decompress(dims->n_head, dims->d_v, dims->kv_rank, n_tok, o_lat, o_dt == MLA_BF16,
                                               w_uv, w_dt == MLA_BF16, out, out_dt == MLA_BF16,
                                               static_cast<hipStream_t>(stream));

@@ -74,6 +74,36 @@ def test_decode_host_validation():
     assert decode(ws_bytes=16, splits=4) == B.MLA_ERR_WORKSPACE
 
 
+def test_decode_refuses_misaligned_pointers():
+    # 16-byte vectors for the queries, cache and outputs; 4-byte words for the
+    # table, lengths and LSE; a 256-byte aligned workspace.
+    odd16 = ctypes.c_void_p(0x1008)
+    odd4 = ctypes.c_void_p(0x1002)
+    assert decode(q=odd16) == B.MLA_ERR_ARG
+    assert decode(kv=odd16) == B.MLA_ERR_ARG
+    assert decode(out=odd16) == B.MLA_ERR_ARG
+    assert decode(bt=odd4) == B.MLA_ERR_ARG
+    assert decode(sl=odd4) == B.MLA_ERR_ARG
+    assert decode(lse=odd4) == B.MLA_ERR_ARG
+    assert decode(ws=ctypes.c_void_p(0x1080)) == B.MLA_ERR_ARG
+    L = mla.lib()
+    assert L.mla_absorb_q(dims(), 4, odd16, FAKE, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_ARG
+    assert L.mla_absorb_q(dims(), 4, FAKE, odd16, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_ARG
+    assert L.mla_absorb_q(dims(), 4, FAKE, FAKE, FAKE, 1, odd16, 1, None) == B.MLA_ERR_ARG
+    assert L.mla_decompress_v(dims(), 4, odd16, 1, FAKE, 1, FAKE, 1, None) == B.MLA_ERR_ARG
+    assert L.mla_decompress_v(dims(), 4, FAKE, 1, FAKE, 1, odd16, 1, None) == B.MLA_ERR_ARG
+
+
+def test_decode_refuses_plans_beyond_32bit_counts():
+    # Workgroup and status-slot counts are 32-bit on the device: a plan whose
+    # count would wrap is refused instead of launching a wrong grid.
+    sz = ctypes.c_size_t()
+    L = mla.lib()
+    big = (65536, 1, 0, 1, 32)  # generic path (float32 geometry): one workgroup per query row
+    assert L.mla_decode_workspace_size(dims(big), 1024, 1, 4096, 16, 1024, ctypes.byref(sz)) == B.MLA_ERR_SHAPE
+    assert decode(dims=dims(big), batch=1024, max_blocks=4096, splits=1024, dt=B.MLA_F32) == B.MLA_ERR_SHAPE
+
+
 def test_workspace_size_explicit_splits():
     sz = ctypes.c_size_t()
     L = mla.lib()
