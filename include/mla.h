@@ -99,24 +99,34 @@ float mla_default_scale(const mla_dims* dims);
  * q_nope [n_tok][n_head][d_nope], q_pe [n_tok][n_head][d_rope] (may be NULL
  * when d_rope == 0), w_uk [n_head][d_nope][kv_rank]: all of type in_dt.
  * q_abs  [n_tok][n_head][kv_rank + d_rope] of type out_dt.
- * Products accumulate in float32.  n_tok == 0 is a no-op.
+ * Products accumulate in float32.  n_tok == 0 is a no-op.  Every tensor
+ * pointer must be 16-byte aligned.
  * Errors: MLA_ERR_NULL, MLA_ERR_DIMS (n_head, d_nope, kv_rank < 1 or d_rope < 0),
- * MLA_ERR_SHAPE (n_tok < 0), MLA_ERR_ARG (bad dtype code), MLA_ERR_HIP. */
+ * MLA_ERR_SHAPE (n_tok < 0), MLA_ERR_ARG (bad dtype code, misaligned pointer),
+ * MLA_ERR_HIP. */
 mla_status mla_absorb_q(const mla_dims* dims, int64_t n_tok, const void* q_nope,
                         const void* q_pe, const void* w_uk, mla_dtype in_dt, void* q_abs,
                         mla_dtype out_dt, void* stream);
 
 /* Phase one of decode (CANN two-phase convention): bytes of device workspace
- * that mla_decode_attention needs for these sizes.  num_splits is the number
- * of KV splits per request (0 = choose automatically for the current device).
+ * that mla_decode_attention needs for these sizes.  num_splits sets how the
+ * cache rows are cut into ranges that run in parallel (0 = choose
+ * automatically for the current device):
+ *   - bf16, kv_rank 512, d_rope 0 or 64, and t_q * n_head >= 128: the 32-row
+ *     tiles of all requests, in request order, are cut into batch * num_splits
+ *     ranges of equal tile count (a length-balanced schedule built on the
+ *     device from seq_lens; a request may span several ranges or share one);
+ *   - otherwise: every request's rows are cut into num_splits ranges of whole
+ *     cache blocks (ranges sized from max_blocks).
  * Errors: MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED
  * (block_size != 16), MLA_ERR_HIP (device query failed, auto mode only). */
 mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t t_q,
                                      int32_t max_blocks, int32_t block_size,
                                      int32_t num_splits, size_t* bytes);
 
-/* The number of KV splits per request mla_decode_attention will use for these
- * sizes (resolves num_splits == 0).  Returns 0 on invalid arguments. */
+/* The total number of KV ranges mla_decode_attention will use for these sizes
+ * with bf16 storage (resolves num_splits == 0; see mla_decode_workspace_size).
+ * Returns 0 on invalid arguments. */
 int32_t mla_decode_resolve_splits(const mla_dims* dims, int32_t batch, int32_t t_q,
                                   int32_t max_blocks, int32_t num_splits);
 
@@ -146,9 +156,12 @@ int32_t mla_decode_resolve_splits(const mla_dims* dims, int32_t batch, int32_t t
  *           it also holds the data-error word read by mla_decode_status.
  * Results do not depend on the block labels; for a fixed num_splits they are
  * bitwise reproducible run to run.  Accumulation is float32 (bf16 products).
+ * Alignment: q_abs, kv_cache and out_lat 16 bytes; block_table, seq_lens and
+ * lse 4 bytes; workspace 256 bytes (allocations from hipMalloc satisfy all).
  * Errors: MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE (batch < 0, t_q < 1,
- * max_blocks < 1, num_blocks < 1, num_splits < 0), MLA_ERR_UNSUPPORTED
- * (block_size != 16), MLA_ERR_ARG (scale not finite or <= 0, bad dtype code),
+ * max_blocks < 1, num_blocks < 1, num_splits < 0, or counts beyond the
+ * device's 32-bit indices), MLA_ERR_UNSUPPORTED (block_size != 16),
+ * MLA_ERR_ARG (scale not finite or <= 0, bad dtype code, misaligned pointer),
  * MLA_ERR_WORKSPACE, MLA_ERR_HIP.  Data errors found on the device (see the
  * MLA_DATA_* bits) do not fail the call: they poison that request's outputs
  * with NaN and are reported by mla_decode_status. */
@@ -214,9 +227,10 @@ mla_status mla_lse_combine(int32_t width, int64_t n_rows, int32_t n_parts, const
  * mla_attend_absorbed, decompress step):
  *   out[n][h][j] = sum_l w_uv[h][j][l] * o_lat[n][h][l]
  * o_lat [n_tok][n_head][kv_rank] type o_dt, w_uv [n_head][d_v][kv_rank] type
- * w_dt, out [n_tok][n_head][d_v] type out_dt.  Float32 accumulation.
+ * w_dt, out [n_tok][n_head][d_v] type out_dt.  Float32 accumulation.  Every
+ * tensor pointer must be 16-byte aligned.
  * Errors: MLA_ERR_NULL, MLA_ERR_DIMS (n_head, d_v, kv_rank < 1), MLA_ERR_SHAPE
- * (n_tok < 0), MLA_ERR_ARG, MLA_ERR_HIP. */
+ * (n_tok < 0), MLA_ERR_ARG (bad dtype code, misaligned pointer), MLA_ERR_HIP. */
 mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_lat,
                             mla_dtype o_dt, const void* w_uv, mla_dtype w_dt, void* out,
                             mla_dtype out_dt, void* stream);

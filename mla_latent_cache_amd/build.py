@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["decode.hip", "gemm.hip", "prolog.hip", "prefill.hip", "mlaprolog.hip", "mla_api.cpp"]
+SOURCES = ["decode.hip", "decode_flat.hip", "gemm.hip", "prolog.hip", "prefill.hip", "mlaprolog.hip", "mla_api.cpp"]
 LIB = os.path.join(PKG, "libmla_amd.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -30,7 +30,7 @@
 // otherwise it writes (o, lse) partials and decode_merge combines them:
 //   M = max_s lse_s, w_s = exp(lse_s - M), o = sum w_s o_s / sum w_s,
 //   lse = M + log sum w_s  (all -inf: zeros and -inf).
-#include "device_common.hpp"
+#include "decode_common.hpp"
 #include "kernels.hpp"
 
 #include <math.h>
@@ -39,28 +39,6 @@
 
 namespace mla {
 namespace {
-
-constexpr uint32_t kNegLen = 0x1u, kLenOverTable = 0x2u, kLenBelowTq = 0x4u, kBadBlock = 0x8u;
-
-// Rows j < x that this rank holds when the rows of a request are dealt to
-// `world` ranks in runs of `il` (row j on rank (j / il) % world, the context-
-// parallel layout whose settings the vLLM CPU MLA backend page names); x
-// itself on a single rank.  A rank keeps its rows in order, so the rows below
-// any global position form a prefix of its own rows.
-__device__ __forceinline__ int64_t held_rows(int64_t x, int world, int rank, int il) {
-  if (world == 1) return x;
-  if (x <= 0) return 0;
-  const int64_t full = x / il, rem = x - full * il;
-  return ((full + world - 1 - rank) / world) * il + (full % world == rank ? rem : 0);
-}
-
-// Data errors of a request of global length Lg holding L rows here.
-__device__ __forceinline__ uint32_t request_flags(int64_t Lg, int64_t L, int t_q, int max_blocks) {
-  if (Lg < 0) return kNegLen;
-  if (L > (int64_t)max_blocks * 16) return kLenOverTable;
-  if (Lg > 0 && Lg < t_q) return kLenBelowTq;
-  return 0u;
-}
 
 // XCD-aware decode of the linear workgroup id (workgroup i runs on XCD i % 8,
 // each XCD with its own L2).  With a batch that is a multiple of 8, every
@@ -104,7 +82,6 @@ __device__ __forceinline__ void write_header(const DecodeArgs& a) {
 
 
 
-constexpr float kSlack = 8.f;   // log2 headroom before the softmax reference moves
 
 // Two 8-byte LDS reads at lds_addr + OFF and + OFF + 32, as separate
 // ds_read_b64 instructions (the compiler would pair them into one

@@ -1,0 +1,723 @@
+// Length-balanced split-KV paged MLA decode for gfx950: bf16 queries and cache,
+// kv_rank 512, rope width 0 or 64, and the merge of the pieces it leaves.
+//
+// What is computed (vllm.cpp "cpu_mla_attn.cpp", MlaDecodeAttentionKernel;
+// memra-engine "mla.rs", MlaInputs causal rule): for request b, query i and
+// head h, scores s_j = scale * <q_abs, row_j> over the full latent row
+// [c_kv | k_pe], softmax over the visible rows j < L - t_q + i + 1, output the
+// softmax-weighted sum of the leading 512 columns of the same rows, and
+// lse = log sum_j exp(s_j).  L == 0 gives zeros and -inf.
+//
+// Work split.  A request of L rows has ceil(L / 32) tiles of 32 rows (two
+// 16-row cache blocks).  The tiles of all requests, in request order, form one
+// sequence of T tiles; range g of G covers tiles [g T / G, (g + 1) T / G), so
+// every workgroup streams the same number of tiles whatever the lengths (the
+// sequence is rebuilt on the device from seq_lens by every workgroup: one
+// load and a wave scan per 64 requests).  Each query tile (qt = 64 or 128
+// query rows x heads of one request) has its own G workgroups, placed so that
+// the query tiles of one range share an XCD and read the cache through one L2.
+// A request inside one range is finished there (final output and LSE);
+// a request cut by a range end leaves float32 (o, lse) pieces, at most two per
+// workgroup (its first and its last request), which decode_flat_merge combines:
+//   M = max lse_k, w_k = exp(lse_k - M), o = sum w_k o_k / sum w_k,
+//   lse = M + log sum w_k  (all -inf: zeros and -inf).
+//
+// Workgroup: four waves, one per SIMD; wave w owns query rows
+// [16 QB w, 16 QB (w + 1)) of the tile over the full row width, so the scores,
+// the online softmax and the probabilities never leave its registers:
+//   * tiles go HBM -> LDS directly (buffer_load ... lds) through a ring of four
+//     tile images, three tiles in flight while one is consumed; one buffer
+//     resource per cache block, sized to the request's valid rows (rows past
+//     the end read as zeros; no address outside a real block is formed);
+//   * S^T = K Q^T with 16x16x32 bf16 MFMA: K as 16-byte LDS reads (one row per
+//     lane), the queries as B operands held in registers for the request;
+//   * online softmax with a delayed maximum (the reference moves only when a
+//     tile's maximum exceeds it by more than kSlack in log2 units);
+//   * the probabilities, packed to bf16, are already the B operand of
+//     O^T = V^T P^T (the 16x16 output layout of S^T holds, per lane, the eight
+//     rows that the B operand's eight k-slots take, and the transposing reads
+//     of V^T use the same row order), so P^T stays in registers;
+//   * V^T comes from the same LDS tile with ds_read_b64_tr_b16.
+// One barrier per tile: after it tile k is resident for every wave and the
+// slot of tile k - 1 is free for tile k + 3.
+#include "decode_common.hpp"
+#include "kernels.hpp"
+
+#include <math.h>
+#include <utility>
+
+namespace mla {
+namespace {
+
+constexpr int kWaves = 8;  // per workgroup, two per SIMD
+constexpr int kRing = 4;   // tile images in LDS
+
+// LDS image of one 32-row tile (two 16-row cache blocks) of latent rows of
+// width D = 512 + D_ROPE, filled by 1 KB wave-loads (64 lanes x 16 bytes).
+// Every row takes 72 16-byte chunk slots (1152 bytes: the whole row at
+// D = 576, the row and 8 empty slots at D = 512), and logical chunk c of row r
+// sits in slot c ^ (r & 7).  With this layout the 16-byte K reads (16 rows of
+// one chunk column) and the transposing V^T reads (4 rows x 32 bytes per 16
+// lanes) are both free of bank conflicts on gfx950 (measured with the LDS
+// bank-conflict counter; the pitch-74 layout with swapped chunk pairs that
+// suits 8-byte K reads gives the 16-byte reads two-way conflicts).
+template <int D_ROPE>
+struct FlatTile {
+  static constexpr int D = 512 + D_ROPE;
+  static constexpr int CH = D / 8;                 // 16-byte chunks of data per row
+  static constexpr int STRIDE = 72;                // chunk slots per row
+  static constexpr int BLK_POS = 16 * STRIDE;      // chunk slots of one block image
+  static constexpr int BLK_LOADS = BLK_POS / 64;   // 1 KB wave-loads per block
+  static constexpr int IMG = 2 * BLK_POS;          // one 32-row tile
+  static constexpr int TILE_LOADS = 2 * BLK_LOADS;
+  static constexpr int KSTEPS = D / 32;            // 32-wide k-steps of q.k
+  static_assert(CH <= STRIDE && BLK_POS % 64 == 0 && TILE_LOADS % 4 == 0, "tile geometry");
+};
+
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// 16-byte / transposing 8-byte LDS reads at a compile-time offset; the result
+// is not ready until a matching lgkm wait.  (Written as assembly so that the
+// waits can be exact: the compiler would wait for every read before its use.)
+template <int OFF>
+__device__ __forceinline__ void lds_b128(uint32_t addr, u32x4& v) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_tr_b64(uint32_t addr, uint2& v) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& v) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "i"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(uint2& x, uint2& y) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(n) for the counts the tile ring uses (n = 0 or a multiple
+// of a wave's per-tile load count, at most two tiles).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 20: wait_vmcnt<20>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// Tiles of a request of global length Lg (L rows held here), 0 for an empty or
+// invalid request; f receives its data-error bits.
+__device__ __forceinline__ int req_tiles(const FlatArgs& a, int64_t Lg, int64_t& L, uint32_t& f) {
+  L = held_rows(Lg, a.dcp_world, a.dcp_rank, a.dcp_interleave);
+  f = request_flags(Lg, L, a.t_q, a.max_blocks);
+  return (f || L <= 0) ? 0 : (int)((L + 31) >> 5);
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The workgroup's place in the tile sequence, computed identically by every
+// wave: T (total tiles), the range [t0, t1) of range g, and the first request
+// this workgroup handles with the index of its first tile.  That request is
+// the first one not entirely before t0, where an empty request whose position
+// is exactly t0 counts as this range's (an empty request belongs to the range
+// holding its position; empty requests at position T belong to the last range).
+struct FlatRange {
+  int64_t T, t0, t1, p_first;
+  int b_first;
+};
+
+__device__ FlatRange flat_range(const FlatArgs& a, int g) {
+  const int lane = threadIdx.x & 63;
+  int64_t acc = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    const int b = base + lane;
+    if (b < a.batch) {
+      int64_t L;
+      uint32_t f;
+      acc += req_tiles(a, a.seq_lens[b], L, f);
+    }
+  }
+  FlatRange r;
+  r.T = uniform64(wave_sum64(acc));
+  r.t0 = (int64_t)g * r.T / a.G;
+  r.t1 = (int64_t)(g + 1) * r.T / a.G;
+  r.b_first = a.batch;
+  r.p_first = r.T;
+  int64_t run = 0;
+  for (int base = 0; base < a.batch; base += 64) {
+    const int b = base + lane;
+    int64_t n = 0;
+    if (b < a.batch) {
+      int64_t L;
+      uint32_t f;
+      n = req_tiles(a, a.seq_lens[b], L, f);
+    }
+    int64_t incl = n;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    incl += run;
+    const int64_t excl = incl - n;
+    const bool before = b < a.batch && incl <= r.t0 && (n > 0 || excl < r.t0);
+    const int cnt = __popcll(__ballot(before));
+    if (cnt < 64) {
+      r.b_first = __builtin_amdgcn_readfirstlane(base + cnt);
+      r.p_first = uniform64(__shfl(excl, cnt, 64));
+      break;
+    }
+    run = __shfl(incl, 63, 64);
+  }
+  return r;
+}
+
+// The range holding tile t (t < T): the largest g with g T / G <= t.
+__device__ __forceinline__ int range_of(int64_t t, int64_t T, int G) { return (int)(((t + 1) * G - 1) / T); }
+
+// A request cursor: request b starts at tile p of the sequence and has n tiles
+// and L rows here.
+struct Cursor {
+  int b;
+  int n;
+  int64_t p, L, Lg;
+  uint32_t f;
+};
+
+__device__ __forceinline__ void cursor_load(const FlatArgs& a, Cursor& c) {
+  const const_i32* sl = (const const_i32*)a.seq_lens;
+  c.Lg = sl[c.b];
+  c.n = req_tiles(a, c.Lg, c.L, c.f);
+}
+
+// Eight waves (two per SIMD), 128 query rows per workgroup: wave w owns query
+// rows [16 w, 16 w + 16) of the workgroup's query tile over the full row width
+// and all 512 value columns.  A request's 128 query rows x heads share every
+// tile image, so its cache rows go HBM -> LDS once; the two waves on a SIMD
+// cover each other's LDS and matrix-core latencies.
+template <int D_ROPE>
+__global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArgs a) {
+  using T = FlatTile<D_ROPE>;
+  constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KS = T::KSTEPS;
+  constexpr int QT = 16 * kWaves;  // query rows per workgroup
+  constexpr int NCT = 32;          // 16-column output tiles of the 512 value columns
+  __shared__ __attribute__((aligned(16))) u32x4 ring[kRing * T::IMG];
+
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.header[0] = kWorkspaceMagic;
+    a.header[1] = (uint32_t)(a.G * a.m_tiles);
+    a.header[2] = (uint32_t)a.G;
+    a.header[3] = (uint32_t)a.batch;
+  }
+  // Workgroup i runs on XCD i % 8: the query tiles of range g all land on XCD g % 8.
+  const int lin = blockIdx.x;
+  const int rest = lin >> 3;
+  const int mt = rest % a.m_tiles;
+  const int g = (rest / a.m_tiles) * 8 + (lin & 7);
+  if (g >= a.G) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  const FlatRange R = flat_range(a, g);
+  const int64_t t0 = R.t0, t1 = R.t1;
+  const bool last_range = g == a.G - 1;
+  if (t0 == t1 && !last_range) {
+    // No tiles and no request here; the merge may still walk over this range
+    // (ranges outnumber tiles), so its first slot reads as an empty piece.
+    const int64_t pidx = ((int64_t)g * a.m_tiles + mt) * 2;
+    for (int i = tid; i < QT; i += 64 * kWaves) a.lse_part[pidx * QT + i] = -INFINITY;
+    if (tid == 0) a.status[(int64_t)g * a.m_tiles + mt] = 0u;
+    return;
+  }
+
+  const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
+  const const_i32* bt_s = (const const_i32*)a.bt;
+  const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
+
+  // Tile loads: wave w issues the 1 KB wave-loads u = w + 8 j of a tile image;
+  // load u covers chunk slots [64 u, 64 u + 64), i.e. block u / BLK_LOADS.
+  constexpr int LJ = (T::TILE_LOADS + kWaves - 1) / kWaves;
+  const int c_w = (T::TILE_LOADS - w + kWaves - 1) / kWaves;  // this wave's loads per tile
+  // Global byte offset (within its block) of this lane's 16 bytes of load u;
+  // padding slots get an offset past any block (they read zeros).
+  auto voff = [&](int u) {
+    // Recomputed at every use from an opaque copy of the lane index, so that
+    // the compiler does not hoist the offsets out of the tile loop (they do
+    // not fit in registers next to the queries and accumulators).
+    int ln;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    const int hb = u / T::BLK_LOADS;
+    const int pos = (u - hb * T::BLK_LOADS) * 64 + ln;
+    const int rl = pos / STRIDE;
+    const int c = (pos - rl * STRIDE) ^ (rl & 7);
+    return c < CH ? (uint32_t)(rl * D + c * 8) * 2u : 0x7ffffff0u;
+  };
+  const uint32_t ring_base = lds_addr(ring);
+
+  // Producer: the tile loads of tile k go out in two steps.  fetch(k) finds
+  // the request holding tile k and issues the scalar loads of its two block
+  // ids; it runs at the end of a tile step, so the loads complete under the
+  // next step's waits.  launch(k) forms one buffer resource per block (sized
+  // to the request's valid rows) and the tile's ring slot, and records in
+  // slot_bad whether a block id of the tile was outside the cache; the next
+  // S step then issues this wave's 1 KB loads one at a time (dma_part), so
+  // that the memory pipeline takes them while the matrix cores work.
+  Cursor prod;
+  prod.b = R.b_first;
+  prod.p = R.p_first;
+  if (prod.b < a.batch) cursor_load(a, prod);
+  int32_t pid[2] = {-1, -1};
+  int pkl = 0;
+  uint32_t slot_bad = 0;
+  auto fetch = [&](int64_t k) {
+    while (k >= prod.p + prod.n) {  // k < T, so a request holding it follows
+      prod.p += prod.n;
+      ++prod.b;
+      cursor_load(a, prod);
+    }
+    pkl = (int)(k - prod.p);
+    const int nblk = (int)((prod.L + 15) >> 4);
+    const const_i32* row = bt_s + (int64_t)prod.b * a.max_blocks;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) pid[hb] = 2 * pkl + hb < nblk ? row[2 * pkl + hb] : -1;
+  };
+  i32x4 lrs[2];
+  uint32_t lbase = 0;
+  auto dma_part = [&](int j) {
+    const int u = w + kWaves * j;
+    const bool in_tile = kWaves * j + kWaves - 1 < T::TILE_LOADS || u < T::TILE_LOADS;
+    const bool blk0 = kWaves * j + kWaves - 1 < T::BLK_LOADS || (kWaves * j < T::BLK_LOADS && u < T::BLK_LOADS);
+    if (in_tile) dma16(blk0 ? lrs[0] : lrs[1], lbase + (uint32_t)u * 1024u, voff(u));
+  };
+  auto launch = [&](int64_t k) {
+    uint32_t badbit = 0;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int64_t left = prod.L - (int64_t)(2 * pkl + hb) * 16;
+      const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
+      const bool ok = (uint32_t)pid[hb] < nb32;
+      if (nvalid > 0 && !ok) badbit = 1u;
+      lrs[hb] = raw_rsrc(kv + (int64_t)(ok ? pid[hb] : 0) * (16 * D), ok ? (uint32_t)(nvalid * D * 2) : 0u);
+    }
+    const uint32_t slot = (uint32_t)((k - t0) & (kRing - 1));
+    slot_bad = (slot_bad & ~(1u << slot)) | (badbit << slot);
+    lbase = ring_base + slot * (uint32_t)(T::IMG * 16);
+  };
+
+  // First three tiles in flight before anything else; the block ids of the
+  // fourth fetched for the first tile step.
+  int64_t k_next = t0;
+  for (int s = 0; s < kRing - 1 && k_next < t1; ++s) {
+    fetch(k_next);
+    launch(k_next++);
+#pragma unroll
+    for (int j = 0; j < LJ; ++j) dma_part(j);
+  }
+  if (k_next < t1) fetch(k_next);
+
+  // Per-lane LDS offsets within a tile image.  The swizzle only permutes
+  // chunks within aligned groups of 8 (128 bytes), so a lane's offset depends
+  // on the k-step (column tile) modulo 2 (4) plus a whole number of groups.
+  // K (A operand of S^T), block rb, k-step ks: row l16, chunk 4 ks + g4.
+  uint32_t k_off[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) k_off[e] = (uint32_t)((l16 * STRIDE + ((4 * e + g4) ^ (l16 & 7))) * 16);
+  // V^T (A operand of O^T), column tile ct: rows 4 g4 + l16 / 4 of each block,
+  // columns 16 ct + 4 (l16 % 4) .. + 3, i.e. chunk 2 ct + (l16 % 4) / 2.
+  const int rr = 4 * g4 + (l16 >> 2);
+  uint32_t v_off[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    v_off[e] = (uint32_t)((rr * STRIDE + ((2 * e + ((l16 & 3) >> 1)) ^ (rr & 7))) * 16 + (l16 & 1) * 8);
+
+  const float sl2 = a.scale * kLog2e;
+  uint32_t wflags = 0;
+  const int ql = 16 * w + l16;   // this lane's query row within the workgroup's tile
+  const int qr = mt * QT + ql;   // and within the request
+  const bool q_ok = qr < a.n_q;
+
+  bf16x8 qf[KS];
+  f32x4 acc[NCT];
+
+  // Writes the lane's query row of request b: the value columns (acc times
+  // inv, or fill_v everywhere) and the LSE, to the final output or to partial
+  // slot `pidx` (-1: final).
+  auto write_row = [&](int b, float inv, float lse_v, bool fill, float fill_v, int64_t pidx) {
+    if (!q_ok) return;
+    if (pidx < 0) {
+      const int64_t orow = (int64_t)b * a.n_q + qr;
+      if (a.out_bf16) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + orow * 512 + 4 * g4;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const f32x4 v = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[ct] * inv;
+          *reinterpret_cast<uint2*>(o + 16 * ct) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      } else {
+        float* o = static_cast<float*>(a.out) + orow * 512 + 4 * g4;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          *reinterpret_cast<f32x4*>(o + 16 * ct) = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[ct] * inv;
+      }
+      if (g4 == 0 && a.lse) a.lse[orow] = lse_v;
+    } else {
+      float* o = a.o_part + (pidx * QT + ql) * 512 + 4 * g4;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        *reinterpret_cast<f32x4*>(o + 16 * ct) = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[ct] * inv;
+      if (g4 == 0) a.lse_part[pidx * QT + ql] = lse_v;
+    }
+  };
+
+  Cursor cons;
+  cons.b = R.b_first;
+  cons.p = R.p_first;
+  for (; cons.b < a.batch; ++cons.b) {
+    cursor_load(a, cons);
+    if (cons.p >= t1 && !last_range) break;
+    const int b = cons.b;
+    if (cons.n == 0) {  // empty or invalid request, owned by this range
+      write_row(b, 0.f, cons.f ? NAN : -INFINITY, true, cons.f ? NAN : 0.f, -1);
+      wflags |= cons.f;
+      if (mt == 0 && tid == 0) *reinterpret_cast<i32x4*>(a.req + 4 * (int64_t)b) = i32x4{-1, -1, 0, 0};
+      continue;
+    }
+    const int64_t ka = cons.p > t0 ? cons.p : t0;
+    const int64_t ke = cons.p + cons.n < t1 ? cons.p + cons.n : t1;
+    const bool first_piece = ka == cons.p;
+    const bool whole = first_piece && ke == cons.p + cons.n;
+    if (first_piece && mt == 0 && tid == 0) {
+      const int g1 = whole ? g : range_of(cons.p + cons.n - 1, R.T, a.G);
+      *reinterpret_cast<i32x4*>(a.req + 4 * (int64_t)b) = i32x4{g, g1, cons.p == t0 ? 0 : 1, 0};
+    }
+
+    // The lane's query as B operands of S^T: lane (l16, g4) holds columns
+    // 32 ks + 8 g4 .. + 7 of query row ql; rows past n_q are zero.
+    {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
+                                                         ((int64_t)b * a.n_q + (q_ok ? qr : 0)) * D + 8 * g4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(q_ok ? src[4 * ks] : u32x4{0u, 0u, 0u, 0u});
+    }
+    // Rows of this request visible to the lane's query (its causal horizon).
+    int hz;
+    {
+      const int64_t h = q_ok ? held_rows(cons.Lg - a.t_q + qr / a.n_head + 1, a.dcp_world, a.dcp_rank,
+                                         a.dcp_interleave)
+                             : 0;
+      hz = (int)(h < cons.L ? h : cons.L);
+    }
+    // The query loads are the only vector-memory loads the compiler tracks in
+    // this loop: wait for them here (with every tile load issued so far), so it
+    // does not put a full wait before every tile's first product.
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m2 = -INFINITY, lsum = 0.f;  // softmax state (log2 units)
+    bool bad = false;
+
+    for (int64_t k = ka; k < ke; ++k) {
+      // Tile k resident: this wave's loads of it are done once at most the
+      // loads of the tiles issued after it (k + 1, k + 2) are outstanding (the
+      // first tile of a request was waited for with the query loads).
+      if (k != ka) wait_vm(c_w * ((k + 1 < t1 ? 1 : 0) + (k + 2 < t1 ? 1 : 0)));
+      barrier_keep_loads();  // tile k visible to all waves; tile k - 1 no longer read
+      const bool loading = k_next < t1;
+      if (loading) launch(k_next++);
+      const int kl = (int)(k - cons.p);
+      const uint32_t slot = (uint32_t)((k - t0) & (kRing - 1));
+      if ((slot_bad >> slot) & 1u) bad = true;
+      const uint32_t img = ring_base + slot * (uint32_t)(T::IMG * 16);
+
+      // S^T of the tile: (k-step, block) pairs I = 2 ks + rb, K reads issued
+      // kAhead pairs ahead of their products; this wave's loads of tile k + 3
+      // go out among them.
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      {
+        constexpr int NP = 2 * KS;
+        constexpr int kAhead = 4;
+        // Pair I: k-step ks = I / 2, block rb = I % 2; 128-byte group ks / 2.
+        const uint32_t kaddr[2] = {img + k_off[0], img + k_off[1]};
+        u32x4 kr[NP];
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (lds_b128<(I % 2) * T::BLK_POS * 16 + 128 * (I / 4)>(kaddr[(I / 2) % 2], kr[I]), ...);
+        }(std::make_integer_sequence<int, kAhead>{});
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (([&] {
+             constexpr int issued = I + kAhead < NP ? I + kAhead : NP;
+             lgkm_wait<issued - 1 - I>(kr[I]);
+             sacc[I % 2] = mfma16x16x32(as_bf16x8(kr[I]), qf[I / 2], sacc[I % 2]);
+             if constexpr (I + kAhead < NP) {
+               constexpr int P = I + kAhead;
+               lds_b128<(P % 2) * T::BLK_POS * 16 + 128 * (P / 4)>(kaddr[(P / 2) % 2], kr[P]);
+             }
+             if constexpr (I % 3 == 1 && I / 3 < LJ) {
+               if (loading) dma_part(I / 3);
+             }
+             __builtin_amdgcn_sched_barrier(0);
+           }()),
+           ...);
+        }(std::make_integer_sequence<int, NP>{});
+      }
+
+      // Online softmax of the lane's query over tile rows 16 rb + 4 g4 + i (the
+      // other twelve rows of each block sit in the lanes l16 + 16 g', g' != g4),
+      // and P^T as the B operand of O^T.
+      float sc[8];
+      float tmax = -INFINITY;
+      const int rbase = 32 * kl + 4 * g4;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = rbase + 16 * rb + i < hz ? sacc[rb][i] * sl2 : -INFINITY;
+          sc[4 * rb + i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = max4rows(tmax);
+      const bool grow = tmax > m2 + kSlack;
+      const float alpha = grow && m2 > -INFINITY ? __builtin_amdgcn_exp2f(m2 - tmax) : 1.f;
+      if (grow) m2 = tmax;
+      const float m_use = m2 == -INFINITY ? 0.f : m2;
+      float pr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+      lsum = lsum * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+      const bf16x8 pB = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] *= alpha;
+      }
+
+      // O^T += V^T P^T, V^T read kAhead column tiles ahead.
+      {
+        constexpr int kAhead = 3;
+        // Column tile ct: 128-byte group ct / 4, lane offset v_off[ct % 4].
+        const uint32_t vaddr[4] = {img + v_off[0], img + v_off[1], img + v_off[2], img + v_off[3]};
+        uint2 vr[NCT][2];
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          ((lds_tr_b64<128 * (I / 4)>(vaddr[I % 4], vr[I][0]),
+            lds_tr_b64<T::BLK_POS * 16 + 128 * (I / 4)>(vaddr[I % 4], vr[I][1])),
+           ...);
+        }(std::make_integer_sequence<int, kAhead>{});
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (([&] {
+             constexpr int issued = I + kAhead < NCT ? I + kAhead : NCT;
+             lgkm_wait<2 * (issued - 1 - I)>(vr[I][0], vr[I][1]);
+             const bf16x8 vA = as_bf16x8(u32x4{vr[I][0].x, vr[I][0].y, vr[I][1].x, vr[I][1].y});
+             acc[I] = mfma16x16x32(vA, pB, acc[I]);
+             if constexpr (I + kAhead < NCT) {
+               constexpr int P = I + kAhead;
+               lds_tr_b64<128 * (P / 4)>(vaddr[P % 4], vr[P][0]);
+               lds_tr_b64<T::BLK_POS * 16 + 128 * (P / 4)>(vaddr[P % 4], vr[P][1]);
+             }
+             __builtin_amdgcn_sched_barrier(0);
+           }()),
+           ...);
+        }(std::make_integer_sequence<int, NCT>{});
+      }
+      if (k_next < t1) fetch(k_next);  // block ids of the tile the next step issues
+    }
+
+    // Finish the piece: 1 / l and the LSE of the lane's query (l summed over
+    // its four lanes), then the final output or a partial slot.
+    const float l = sum4rows(lsum);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse_v = bad ? NAN : (l > 0.f ? (m2 + __log2f(l)) * kLn2 : -INFINITY);
+    if (bad) wflags |= kBadBlock;
+    const int64_t pidx = whole ? -1 : ((int64_t)g * a.m_tiles + mt) * 2 + (cons.p <= t0 ? 0 : 1);
+    write_row(b, inv, lse_v, bad, NAN, pidx);
+    cons.p += cons.n;
+  }
+  if (tid == 0) a.status[(int64_t)g * a.m_tiles + mt] = wflags;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the pieces of the requests cut by range ends.  W waves per query
+// row (one row per workgroup when W > 1, else kMergeRows rows of one wave):
+// wave v sums the contiguous pieces [v P / W, (v + 1) P / W) of the row's P
+// pieces, and the wave sums are added in wave order through LDS, so the result
+// does not depend on timing.  Lane l owns value columns 4 l .. + 3 and
+// 256 + 4 l .. + 3.  Pieces are read eight at a time.
+// ---------------------------------------------------------------------------
+constexpr int kMergeRows = 4;
+
+__device__ __forceinline__ float wmax(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wsum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int W>
+__global__ __launch_bounds__(64 * (W > 1 ? W : kMergeRows)) void decode_flat_merge(const FlatArgs a) {
+  __shared__ float red[W > 1 ? W : 1][2];
+  __shared__ __attribute__((aligned(16))) f32x4 part[W > 1 ? W : 1][2][64];
+  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6;
+  const int64_t qrow = W > 1 ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kMergeRows + v;
+  if (qrow >= (int64_t)a.batch * a.n_q) return;
+  const int b = (int)(qrow / a.n_q);
+  const int q = (int)(qrow - (int64_t)b * a.n_q);
+  const i32x4 info = *reinterpret_cast<const i32x4*>(a.req + 4 * (int64_t)b);
+  const int g0 = info[0], g1 = info[1], s0 = info[2];
+  if (g0 < 0 || g0 == g1) return;  // written by the split kernel
+  const int mt = q / a.qt, ql = q - mt * a.qt;
+  const int P = g1 - g0 + 1;
+  auto pidx = [&](int k) { return ((int64_t)(g0 + k) * a.m_tiles + mt) * 2 + (k == 0 ? s0 : 0); };
+  auto lse_of = [&](int k) { return a.lse_part[pidx(k) * a.qt + ql]; };
+
+  const int wv = W > 1 ? v : 0;
+  const int k0 = (int)((int64_t)P * wv / W), k1 = (int)((int64_t)P * (wv + 1) / W);
+  // Maximum LSE and NaN over all pieces (every wave scans all of them).
+  float mx = -INFINITY;
+  bool nan_seen = false;
+  for (int k = lane; k < P; k += 64) {
+    const float x = lse_of(k);
+    nan_seen |= isnan(x);
+    mx = fmaxf(mx, x);
+  }
+  const float M = wmax(mx);
+  const bool any_nan = __ballot(nan_seen) != 0;
+  float wp = 0.f;
+  if (M != -INFINITY)
+    for (int k = lane; k < P; k += 64) {
+      const float x = lse_of(k);
+      wp += x == -INFINITY ? 0.f : __expf(x - M);
+    }
+  const float wtot = wsum(wp);
+  const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
+
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+  if (M != -INFINITY) {
+    for (int k = k0; k < k1; k += 8) {
+      float wk[8];
+      f32x4 x0[8], x1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kk = k + u < k1 ? k + u : k1 - 1;
+        const int64_t base = (pidx(kk) * a.qt + ql) * 512;
+        wk[u] = lse_of(kk);
+        x0[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 4 * lane);
+        x1[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 256 + 4 * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool live = k + u < k1 && wk[u] != -INFINITY;  // an empty piece may hold anything
+        const float wgt = live ? __expf(wk[u] - M) : 0.f;
+        o0 += wgt * (live ? x0[u] : f32x4{0.f, 0.f, 0.f, 0.f});
+        o1 += wgt * (live ? x1[u] : f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    }
+  }
+  if constexpr (W > 1) {
+    part[v][0][lane] = o0;
+    part[v][1][lane] = o1;
+    __syncthreads();
+    if (v != 0) return;
+    o0 = o1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      o0 += part[i][0][lane];
+      o1 += part[i][1][lane];
+    }
+  }
+  const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+  const f32x4 r0 = any_nan ? nan4 : o0 * inv, r1 = any_nan ? nan4 : o1 * inv;
+  if (a.out_bf16) {
+    uint16_t* o = static_cast<uint16_t*>(a.out) + qrow * 512;
+    *reinterpret_cast<uint2*>(o + 4 * lane) = uint2{pack_bf16x2(r0[0], r0[1]), pack_bf16x2(r0[2], r0[3])};
+    *reinterpret_cast<uint2*>(o + 256 + 4 * lane) = uint2{pack_bf16x2(r1[0], r1[1]), pack_bf16x2(r1[2], r1[3])};
+  } else {
+    float* o = static_cast<float*>(a.out) + qrow * 512;
+    *reinterpret_cast<f32x4*>(o + 4 * lane) = r0;
+    *reinterpret_cast<f32x4*>(o + 256 + 4 * lane) = r1;
+  }
+  if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wtot));
+  (void)red;
+}
+
+}  // namespace
+
+bool flat_supported(int kv_rank, int d_rope, bool bf16) { return bf16 && kv_rank == 512 && (d_rope == 0 || d_rope == 64); }
+
+int64_t flat_auto_ranges(int n_head, int batch, int t_q, int max_blocks, int cus) {
+  const int n_q = t_q * n_head;
+  const int m_tiles = (n_q + 127) / 128;
+  int64_t G = cus / m_tiles;
+  if (G < 1) G = 1;
+  const int64_t max_tiles = (int64_t)(batch > 0 ? batch : 1) * ((max_blocks + 1) / 2);
+  return G < max_tiles ? G : max_tiles;
+}
+
+FlatPlan flat_plan(int n_head, int d_rope, int batch, int t_q, int max_blocks, int64_t ranges) {
+  (void)d_rope;
+  FlatPlan p = {};
+  const int64_t n_q = (int64_t)t_q * n_head;
+  // 128 query rows per workgroup (eight waves) from 128 query rows per
+  // request on, else 64 (four waves); the query tiles of one range share an
+  // XCD, so a cache tile is fetched from HBM once and from L2 by the rest.
+  p.qb = kWaves;  // waves per workgroup
+  p.qt = 16 * kWaves;
+  p.m_tiles = (int)((n_q + p.qt - 1) / p.qt);
+  const int64_t G = ranges < 1 ? 1 : ranges;
+  // Device arithmetic: (t + 1) * G with t < T <= batch * ceil(max_blocks / 2)
+  // in 64 bits, and workgroup and slot counts in 32 bits.
+  const int64_t max_tiles = (int64_t)(batch > 0 ? batch : 1) * ((max_blocks + 1) / 2);
+  const int64_t wgs = (G + 7) / 8 * 8 * p.m_tiles;
+  p.ok = G <= (1 << 24) && max_tiles <= ((int64_t)1 << 38) && wgs <= INT32_MAX;
+  if (!p.ok) return p;
+  p.G = (int)G;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t n_status = (size_t)G * p.m_tiles;
+  p.req_off = al(kHeaderBytes + n_status * 4);
+  p.lse_off = al(p.req_off + (size_t)(batch > 0 ? batch : 1) * 16);
+  const size_t slots = (size_t)G * p.m_tiles * 2 * p.qt;
+  p.o_off = al(p.lse_off + slots * 4);
+  p.bytes = al(p.o_off + slots * 512 * 4);
+  return p;
+}
+
+hipError_t launch_decode_flat(const FlatArgs& a, int d_rope, int qb, hipStream_t stream) {
+  const int grid = (a.G + 7) / 8 * 8 * a.m_tiles;
+  if (qb != kWaves) return hipErrorInvalidValue;
+  if (d_rope == 64)
+    hipLaunchKernelGGL(decode_flat_mfma<64>, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_flat_mfma<0>, dim3(grid), dim3(64 * kWaves), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.batch == 0 || a.G == 1) return e;
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  if (rows > INT32_MAX) return hipErrorInvalidConfiguration;
+  // Many pieces per request on average: one 16-wave workgroup per row.
+  if ((int64_t)a.G >= 32 * (int64_t)a.batch) {
+    hipLaunchKernelGGL(decode_flat_merge<16>, dim3((unsigned)rows), dim3(64 * 16), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(decode_flat_merge<1>, dim3((unsigned)((rows + kMergeRows - 1) / kMergeRows)),
+                       dim3(64 * kMergeRows), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla

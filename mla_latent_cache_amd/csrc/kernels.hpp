@@ -50,6 +50,52 @@ struct Plan {
   size_t lse_off, o_off, bytes;
 };
 
+// Length-balanced decode (bf16, kv_rank 512, rope width 0 or 64).  The
+// 32-row tiles of all requests, in request order, form one sequence of T
+// tiles per query tile; range g of G covers tiles [g T / G, (g + 1) T / G),
+// so every workgroup streams the same number of tiles whatever the lengths.
+// A request that falls in one range is finished by its workgroup; the pieces
+// of a request cut by range ends are merged by decode_flat_merge.
+// Workspace:
+//   [0, 256)           header: magic, number of status slots, ranges, batch
+//   [256, ...)         one uint32 data-error word per workgroup (G * m_tiles)
+//   then (256-aligned) int32x4 per request: first and last range holding it,
+//                      partial slot of the first piece
+//   then (256-aligned) lse partials f32 [G][m_tiles][2][qt]
+//   then (256-aligned) o partials   f32 [G][m_tiles][2][qt][512]
+struct FlatArgs {
+  const void* q;           // [B][t_q][H][D]
+  const void* kv;          // [num_blocks][16][D]
+  const int32_t* bt;       // [B][max_blocks]
+  const int32_t* seq_lens; // [B]
+  void* out;               // [B][t_q][H][512]
+  float* lse;              // [B][t_q][H] or null
+  float* lse_part;
+  float* o_part;
+  int32_t* req;            // [B][4]
+  uint32_t* header;
+  uint32_t* status;        // [G * m_tiles]
+  int64_t num_blocks;
+  int batch, t_q, n_head, max_blocks, n_q;
+  int G;                   // ranges per query tile
+  int m_tiles, qt;         // query tiles per request, query rows per tile
+  float scale;
+  int out_bf16;
+  int dcp_world, dcp_rank, dcp_interleave;
+};
+
+struct FlatPlan {
+  int G, m_tiles, qt, qb;  // ranges, query tiles, rows per tile, waves per workgroup
+  bool ok;
+  size_t req_off, lse_off, o_off, bytes;
+};
+
+bool flat_supported(int kv_rank, int d_rope, bool bf16);
+FlatPlan flat_plan(int n_head, int d_rope, int batch, int t_q, int max_blocks, int64_t ranges);
+// Ranges that give one workgroup per compute unit (at most one per tile).
+int64_t flat_auto_ranges(int n_head, int batch, int t_q, int max_blocks, int cus);
+hipError_t launch_decode_flat(const FlatArgs& a, int d_rope, int qb, hipStream_t stream);
+
 // Kernel selection and workspace layout for a decode call.
 Plan decode_plan(int n_head, int kv_rank, int d_rope, int batch, int t_q, int max_blocks,
                  int splits, bool bf16);

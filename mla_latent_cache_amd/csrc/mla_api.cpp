@@ -68,6 +68,13 @@ bool mfma_path(const mla_dims* d, bool bf16) {
   return bf16 && d->kv_rank == 512 && (d->d_rope == 0 || d->d_rope == 64);
 }
 
+// The length-balanced kernel (128 query rows per workgroup) from 128 query
+// rows per request on; below that the per-request split kernel, whose
+// workgroups hold 64 query rows.
+bool flat_path(const mla_dims* d, int t_q, bool bf16) {
+  return mla::flat_supported(d->kv_rank, d->d_rope, bf16) && (int64_t)t_q * d->n_head >= 128;
+}
+
 mla_status resolve(const mla_dims* d, int batch, int t_q, int max_blocks, int num_splits, bool bf16,
                    int* splits) {
   if (num_splits > 0) {
@@ -119,14 +126,33 @@ mla_status mla_absorb_q(const mla_dims* dims, int64_t n_tok, const void* q_nope,
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// Tile ranges of the length-balanced path: num_splits ranges per request on
+// average (batch * num_splits in all), or one workgroup per compute unit.
+static mla_status flat_ranges(const mla_dims* d, int batch, int t_q, int max_blocks, int num_splits, int64_t* G) {
+  if (num_splits > 0) {
+    *G = (int64_t)(batch > 0 ? batch : 1) * num_splits;
+    return MLA_OK;
+  }
+  int cus = 0;
+  if (device_cus(&cus) != 0) return MLA_ERR_HIP;
+  *G = mla::flat_auto_ranges(d->n_head, batch, t_q, max_blocks, cus);
+  return MLA_OK;
+}
+
 int32_t mla_decode_resolve_splits(const mla_dims* dims, int32_t batch, int32_t t_q, int32_t max_blocks,
                                   int32_t num_splits) {
   if (check_decode_dims(dims) != MLA_OK || batch < 0 || t_q < 1 || max_blocks < 1 || num_splits < 0) return 0;
+  if (flat_path(dims, t_q, true)) {
+    int64_t G = 0;
+    if (flat_ranges(dims, batch, t_q, max_blocks, num_splits, &G) != MLA_OK) return 0;
+    const mla::FlatPlan f = mla::flat_plan(dims->n_head, dims->d_rope, batch, t_q, max_blocks, G);
+    return f.ok ? f.G : 0;
+  }
   int splits = 0;
   if (resolve(dims, batch, t_q, max_blocks, num_splits, true, &splits) != MLA_OK) return 0;
   const mla::Plan p = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
                                        true);
-  return p.splits;
+  return p.ok && (int64_t)batch * p.splits <= INT32_MAX ? batch * p.splits : 0;
 }
 
 mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_t t_q, int32_t max_blocks,
@@ -136,16 +162,28 @@ mla_status mla_decode_workspace_size(const mla_dims* dims, int32_t batch, int32_
   if (!bytes) return MLA_ERR_NULL;
   if (batch < 0 || t_q < 1 || max_blocks < 1 || num_splits < 0) return MLA_ERR_SHAPE;
   if (block_size != 16) return MLA_ERR_UNSUPPORTED;
-  int splits = 0;
-  const mla_status r = resolve(dims, batch, t_q, max_blocks, num_splits, true, &splits);
-  if (r != MLA_OK) return r;
-  // The float32 and bfloat16 paths share one layout; size for the larger.
-  const mla::Plan p1 = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
-                                        true);
-  const mla::Plan p2 = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
-                                        false);
-  if (!p1.ok || !p2.ok) return MLA_ERR_SHAPE;
-  *bytes = p1.bytes > p2.bytes ? p1.bytes : p2.bytes;
+  // The float32 and bfloat16 calls of one geometry may take different paths;
+  // size for the larger.
+  size_t need = 0;
+  for (const bool bf16 : {false, true}) {
+    if (bf16 && flat_path(dims, t_q, true)) continue;
+    int splits = 0;
+    const mla_status r = resolve(dims, batch, t_q, max_blocks, num_splits, bf16, &splits);
+    if (r != MLA_OK) return r;
+    const mla::Plan p = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits,
+                                         mfma_path(dims, bf16));
+    if (!p.ok) return MLA_ERR_SHAPE;
+    if (p.bytes > need) need = p.bytes;
+  }
+  if (flat_path(dims, t_q, true)) {
+    int64_t G = 0;
+    const mla_status rf = flat_ranges(dims, batch, t_q, max_blocks, num_splits, &G);
+    if (rf != MLA_OK) return rf;
+    const mla::FlatPlan f = mla::flat_plan(dims->n_head, dims->d_rope, batch, t_q, max_blocks, G);
+    if (!f.ok) return MLA_ERR_SHAPE;
+    if (f.bytes > need) need = f.bytes;
+  }
+  *bytes = need;
   return MLA_OK;
 }
 
@@ -171,15 +209,55 @@ static mla_status decode_impl(const mla_dims* dims, float scale, int32_t batch, 
   if (!mfma && dims->kv_rank > 1024) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)batch * t_q * dims->n_head > 2147483647LL) return MLA_ERR_SHAPE;
 
+  size_t need = 0;
+  const mla_status ws = mla_decode_workspace_size(dims, batch, t_q, max_blocks, block_size, num_splits, &need);
+  if (ws != MLA_OK) return ws;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(workspace);
+
+  if (flat_path(dims, t_q, bf16)) {
+    int64_t G = 0;
+    const mla_status rf = flat_ranges(dims, batch, t_q, max_blocks, num_splits, &G);
+    if (rf != MLA_OK) return rf;
+    const mla::FlatPlan f = mla::flat_plan(dims->n_head, dims->d_rope, batch, t_q, max_blocks, G);
+    if (!f.ok) return MLA_ERR_SHAPE;
+    mla::FlatArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q_abs;
+    a.kv = kv_cache;
+    a.bt = block_table;
+    a.seq_lens = seq_lens;
+    a.out = out_lat;
+    a.lse = lse;
+    a.header = reinterpret_cast<uint32_t*>(wsb);
+    a.status = reinterpret_cast<uint32_t*>(wsb + mla::kHeaderBytes);
+    a.req = reinterpret_cast<int32_t*>(wsb + f.req_off);
+    a.lse_part = reinterpret_cast<float*>(wsb + f.lse_off);
+    a.o_part = reinterpret_cast<float*>(wsb + f.o_off);
+    a.num_blocks = num_blocks;
+    a.batch = batch;
+    a.t_q = t_q;
+    a.n_head = dims->n_head;
+    a.max_blocks = max_blocks;
+    a.n_q = t_q * dims->n_head;
+    a.G = f.G;
+    a.m_tiles = f.m_tiles;
+    a.qt = f.qt;
+    a.scale = scale;
+    a.out_bf16 = out_dt == MLA_BF16;
+    a.dcp_world = dcp_world;
+    a.dcp_rank = dcp_rank;
+    a.dcp_interleave = dcp_interleave;
+    const hipError_t e = mla::launch_decode_flat(a, dims->d_rope, f.qb, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  }
+
   int splits = 0;
   const mla_status r = resolve(dims, batch, t_q, max_blocks, num_splits, bf16, &splits);
   if (r != MLA_OK) return r;
   const mla::Plan p = mla::decode_plan(dims->n_head, dims->kv_rank, dims->d_rope, batch, t_q, max_blocks, splits, bf16);
   if (!p.ok) return MLA_ERR_SHAPE;
-  size_t need = 0;
-  const mla_status ws = mla_decode_workspace_size(dims, batch, t_q, max_blocks, block_size, splits, &need);
-  if (ws != MLA_OK) return ws;
-  if (workspace_bytes < need || workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < p.bytes) return MLA_ERR_WORKSPACE;
 
   mla::DecodeArgs a;
   memset(&a, 0, sizeof a);
@@ -189,7 +267,6 @@ static mla_status decode_impl(const mla_dims* dims, float scale, int32_t batch, 
   a.seq_lens = seq_lens;
   a.out = out_lat;
   a.lse = lse;
-  char* wsb = static_cast<char*>(workspace);
   a.header = reinterpret_cast<uint32_t*>(wsb);
   a.status = reinterpret_cast<uint32_t*>(wsb + mla::kHeaderBytes);
   a.lse_part = reinterpret_cast<float*>(wsb + p.lse_off);

@@ -117,10 +117,14 @@ def test_workspace_size_explicit_splits():
     assert L.mla_decode_workspace_size(dims(), 32, 1, 256, 8, 8, ctypes.byref(sz)) == B.MLA_ERR_UNSUPPORTED
     assert L.mla_decode_workspace_size(dims(), 32, 0, 256, 16, 8, ctypes.byref(sz)) == B.MLA_ERR_SHAPE
     assert L.mla_decode_workspace_size(dims(), 32, 1, 256, 16, 8, None) == B.MLA_ERR_NULL
-    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 8) == 8
-    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 7) == 7   # 37 blocks per range, 7 ranges
-    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 500) == 256
+    # bf16 MFMA geometry: the batch's tiles are cut into batch * num_splits ranges
+    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 8) == 256
+    assert L.mla_decode_resolve_splits(dims(), 32, 1, 256, 7) == 224
     assert L.mla_decode_resolve_splits(dims(), 32, 0, 256, 8) == 0
+    # other geometries: whole-block ranges of every request (37 blocks per range, 7 ranges)
+    tiny = (4, 16, 8, 16, 32)
+    assert L.mla_decode_resolve_splits(dims(tiny), 32, 1, 256, 7) == 32 * 7
+    assert L.mla_decode_resolve_splits(dims(tiny), 32, 1, 256, 500) == 32 * 256
 
 
 def test_absorb_and_decompress_host_validation():

@@ -1,9 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
 
 Small cases compare every output element; the full-size workloads run in
-the benchmark's launch configuration (automatic split count) and compare a
-seeded sample of (request, query, head) outputs that the oracle computes one
-by one.  Property tests cover split invariance, determinism, block relabelling,
+the benchmark's launch configuration (automatic split count) and compare every
+output (the DeepSeek-shaped one: every head of twelve requests, among them the
+longest, the shortest and both empty ones).  Property tests cover split invariance, determinism, block relabelling,
 the value slice, the causal mask, empty requests and device-side data errors.
 """
 import numpy as np
@@ -199,35 +199,96 @@ def test_hip_graph_replay_matches_eager():
 # --------------------------------------------------------------------------
 # Full-size workloads, launch configuration of the benchmark, sampled outputs
 # --------------------------------------------------------------------------
-FULL = {
-    "glm52_decode": dict(n=96, naive=2),
-    "dsv3_ragged": dict(n=160, naive=0),
-    "glm52_causal_tq4": dict(n=96, naive=2),
-    "nope_long": dict(n=64, naive=0),
-    "nope_wide": dict(n=96, naive=2),
-}
+# Full-size workloads and the number of sampled items also checked against
+# the naive (per-head decompression) form.
+FULL = {"glm52_decode": 2, "dsv3_ragged": 0, "glm52_causal_tq4": 2, "nope_long": 0, "nope_wide": 2}
 
 
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled(name):
+def test_full_size(name):
+    # Every (request, query, head) output of the GLM-5.2, causal and NoPE
+    # workloads; for the DeepSeek-shaped one, every head of the longest, the
+    # shortest non-empty, both empty and eight seeded other requests.
     spec = mi.SPECS[name]
     case = mi.make_case(spec)
     res = run(DeviceCase(case), num_splits=0)
     assert res["status"] == 0
-    must = []
+    sel = None
     if name == "dsv3_ragged":
-        longest = int(np.argmax(case.seq_lens))
-        must = [(0, 0, 0), (0, 0, 127), (63, 0, 5), (longest, 0, 0), (longest, 0, 127)]
-    if spec.t_q > 1:
-        must = [(0, i, h) for i in range(spec.t_q) for h in (0, 63)]
-    sel = mi.sample_items(spec.seed, spec.batch, spec.t_q, spec.n_head, FULL[name]["n"], must=must)
-    full_compare(case, res, sel=sel, naive_items=FULL[name]["naive"])
+        lens = case.seq_lens.astype(np.int64)
+        longest = int(np.argmax(lens))
+        shortest = int(np.argmin(np.where(lens > 0, lens, np.iinfo(np.int64).max)))
+        others = [int(b) for b in np.argsort(mi.draws(mi.tensor_key(spec.seed, "test_requests"), 0, spec.batch))
+                  if b not in (0, 63, longest, shortest)][:8]
+        reqs = sorted({0, 63, longest, shortest, *others})
+        sel = np.array([(b, 0, h) for b in reqs for h in range(spec.n_head)], dtype=np.int32)
+    naive = mi.sample_items(spec.seed, spec.batch, spec.t_q, spec.n_head, FULL[name]) if FULL[name] else None
+    full_compare(case, res, sel=sel, naive_items=0)
+    if naive is not None:
+        d = oracle_dims(spec)
+        out_n, _, _ = oracle.attend_naive(d, spec.t_q, case.q_nope, case.q_pe, case.w_uk, case.w_uv, paged(case),
+                                          case.scale, sel=naive)
+        assert_close(to_host(res["out"]).reshape(-1, spec.d_v)[flat_index(spec, naive)], out_n, spec.dtype,
+                     "out vs naive form")
     if name == "dsv3_ragged":  # every head of the two empty requests
         o = to_host(res["o_lat"])
         lse = to_host(res["lse"])
         for b in (0, 63):
             assert np.all(o[b] == 0.0) and np.all(np.isneginf(lse[b]))
     assert np.isfinite(to_host(res["o_lat"])[case.seq_lens > 0]).all()
+
+
+def test_one_long_request_and_many_short_every_element():
+    # The length-balanced schedule: one 32768-row request among 63 short ones
+    # (some empty) is cut across many workgroups while the short ones are
+    # finished whole; every output element is compared.
+    short = [int(x) for x in (mi.uniforms(mi.tensor_key(77, "short_lens"), 0, 63) * 301).astype(np.int64)]
+    short[5] = short[40] = 0
+    lens = tuple([32768] + short)
+    spec = spec_small("dsv3_long_short", "dsv3_ragged", batch=64, fixed_lens=lens, max_blocks=2048,
+                      lengths="fixed", zero_requests=())
+    case = mi.make_case(spec)
+    for k in (0, 2):
+        res = run(DeviceCase(case), num_splits=k)
+        assert res["status"] == 0
+        full_compare(case, res)
+
+
+@pytest.mark.parametrize("batch", [8, 16])
+@pytest.mark.parametrize("num_splits", [2, 5, 16])
+def test_batch_multiple_of_8_every_element(batch, num_splits):
+    # With a batch that is a multiple of 8 the split kernel and the merge map
+    # request b to XCD b % 8; every element is compared.
+    lens = tuple(17 + (97 * b) % 700 for b in range(batch))
+    spec = spec_small(f"glm52_b{batch}", "glm52_decode", batch=batch, fixed_lens=lens, max_blocks=48)
+    case = mi.make_case(spec)
+    res = run(DeviceCase(case), num_splits=num_splits)
+    assert res["status"] == 0
+    full_compare(case, res)
+
+
+def test_flat_schedule_split_invariance_and_determinism():
+    # 128 query rows per request (the length-balanced kernel): results for
+    # different range counts (including many more ranges than tiles, which
+    # leaves ranges empty) agree within rounding, and each is reproducible.
+    spec = spec_small("dsv3_mid", "dsv3_ragged", batch=5, fixed_lens=(700, 0, 1000, 33, 257), max_blocks=64,
+                      lengths="fixed", zero_requests=())
+    case = mi.make_case(spec)
+    dc = DeviceCase(case)
+    outs = {}
+    for k in (1, 2, 7, 0, 64):
+        r1 = run(dc, num_splits=k, out_dtype=torch.float32)
+        r2 = run(dc, num_splits=k, out_dtype=torch.float32)
+        assert r1["status"] == 0
+        assert torch.equal(r1["o_lat"], r2["o_lat"]) and torch.equal(r1["lse"], r2["lse"]), k
+        outs[k] = (to_host(r1["o_lat"]), to_host(r1["lse"]))
+    ref, lref = outs[1]
+    fin = np.isfinite(lref)
+    for k, (o, l) in outs.items():
+        assert np.abs(o - ref).max() <= 2e-3 * np.abs(ref).max(), k
+        assert np.array_equal(np.isneginf(l), np.isneginf(lref))
+        assert np.abs(l[fin] - lref[fin]).max() <= 1e-4 * max(1.0, np.abs(lref[fin]).max()), k
+    full_compare(case, run(dc, num_splits=64))
 
 
 # --------------------------------------------------------------------------
