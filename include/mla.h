@@ -173,6 +173,27 @@ mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch
                                 float* lse, void* workspace, size_t workspace_bytes,
                                 int32_t num_splits, void* stream);
 
+/* mla_decode_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, the same results bit for bit.
+ * The workspace is a library-owned scratch array of 160 MiB in device memory,
+ * one copy per GPU, held until the process ends; the call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Every call on one GPU uses
+ * that GPU's copy: calls that overlap on one GPU (concurrent streams, or
+ * threads) race and give undefined results; calls in one stream order are
+ * safe.  The device status words live in that scratch and are not readable
+ * through mla_decode_status; data errors still poison the affected requests'
+ * outputs with NaN.
+ * Errors: as mla_decode_attention, plus MLA_ERR_WORKSPACE when the call would
+ * need more than 160 MiB (mla_decode_workspace_size for the same arguments
+ * gives the need), MLA_ERR_HIP when the scratch address cannot be obtained. */
+mla_status mla_decode_attention_noalloc(const mla_dims* dims, float scale, int32_t batch, int32_t t_q,
+                                        const void* q_abs, const void* kv_cache, mla_dtype dt,
+                                        int64_t num_blocks, int32_t block_size,
+                                        const int32_t* block_table, int32_t max_blocks,
+                                        const int32_t* seq_lens, void* out_lat, mla_dtype out_dt,
+                                        float* lse, int32_t num_splits, void* stream);
+
 /* One rank's share of decode context parallelism (the vLLM CPU MLA backend
  * page, CPUMLAImpl construction, names the settings dcp_world_size and
  * cp_kv_cache_interleave_size; the pages print no distributed kernel, so the

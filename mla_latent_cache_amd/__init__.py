@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     mla_cache_append,
     mla_decode_attention,
     mla_decode_attention_dcp,
+    mla_decode_attention_noalloc,
     mla_decode_resolve_splits,
     mla_decode_status,
     mla_decode_workspace_size,

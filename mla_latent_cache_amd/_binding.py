@@ -26,7 +26,7 @@ EXPORTS = ("mla_default_scale", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode_resolve_splits", "mla_decode_attention", "mla_decompress_v",
            "mla_decode_status", "mla_status_string", "mla_cache_append", "mla_prefill_workspace_size",
            "mla_prefill_attention", "mla_decode_attention_dcp", "mla_lse_combine", "mla_prolog_workspace_size",
-           "mla_prolog")
+           "mla_prolog", "mla_decode_attention_noalloc")
 
 
 class MlaError(RuntimeError):
@@ -67,6 +67,9 @@ def lib():
     L.mla_decode_attention.restype = ctypes.c_int
     L.mla_decode_attention.argtypes = [P, f32, i32, i32, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
                                        vp, ctypes.c_int, vp, vp, sz, i32, vp]
+    L.mla_decode_attention_noalloc.restype = ctypes.c_int
+    L.mla_decode_attention_noalloc.argtypes = [P, f32, i32, i32, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
+                                               vp, ctypes.c_int, vp, i32, vp]
     L.mla_decode_attention_dcp.restype = ctypes.c_int
     L.mla_decode_attention_dcp.argtypes = [P, f32, i32, i32, vp, vp, ctypes.c_int, i64, i32, vp, i32, vp,
                                            i32, i32, i32, vp, ctypes.c_int, vp, vp, sz, i32, vp]
@@ -189,6 +192,18 @@ def mla_decode_attention(dims: DimsLike, scale: float, q_abs, kv_cache, block_ta
         int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]),
         _ptr(seq_lens), _ptr(out_lat), _dt(out_lat), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), int(num_splits), _stream(stream)))
+
+
+def mla_decode_attention_noalloc(dims: DimsLike, scale: float, q_abs, kv_cache, block_table, seq_lens, out_lat,
+                                 lse=None, num_splits: int = 0, stream=None) -> None:
+    """mla_decode_attention with the library's own device scratch as the
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    d = as_dims(dims)
+    B, t_q = int(q_abs.shape[0]), int(q_abs.shape[1])
+    _check("mla_decode_attention_noalloc", lib().mla_decode_attention_noalloc(
+        ctypes.byref(d), float(scale), B, t_q, _ptr(q_abs), _ptr(kv_cache), _dt(kv_cache),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]), _ptr(block_table), int(block_table.shape[1]),
+        _ptr(seq_lens), _ptr(out_lat), _dt(out_lat), _ptr(lse), int(num_splits), _stream(stream)))
 
 
 def mla_decode_attention_dcp(dims: DimsLike, scale: float, q_abs, kv_cache, block_table, seq_lens, dcp_world: int,

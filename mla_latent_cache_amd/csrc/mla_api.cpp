@@ -10,7 +10,32 @@
 
 #include "kernels.hpp"
 
+#include <mutex>
+
 namespace {
+
+// Device scratch of mla_decode_attention_noalloc: one copy per GPU, held until
+// the process ends.  Host code never uses the array's name as an address; the
+// address of the current device's copy comes from hipGetSymbolAddress, once
+// per device, and every later use goes through that pointer.
+constexpr size_t kNoAllocScratchBytes = (size_t)160 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+// The current device's scratch address, or null on failure.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool dt_ok(mla_dtype d) { return d == MLA_F32 || d == MLA_BF16; }
 
@@ -301,6 +326,21 @@ mla_status mla_decode_attention(const mla_dims* dims, float scale, int32_t batch
                                 size_t workspace_bytes, int32_t num_splits, void* stream) {
   return decode_impl(dims, scale, batch, t_q, q_abs, kv_cache, dt, num_blocks, block_size, block_table, max_blocks,
                      seq_lens, 1, 0, 1, out_lat, out_dt, lse, workspace, workspace_bytes, num_splits, stream);
+}
+
+mla_status mla_decode_attention_noalloc(const mla_dims* dims, float scale, int32_t batch, int32_t t_q,
+                                        const void* q_abs, const void* kv_cache, mla_dtype dt, int64_t num_blocks,
+                                        int32_t block_size, const int32_t* block_table, int32_t max_blocks,
+                                        const int32_t* seq_lens, void* out_lat, mla_dtype out_dt, float* lse,
+                                        int32_t num_splits, void* stream) {
+  size_t need = 0;
+  const mla_status ws = mla_decode_workspace_size(dims, batch, t_q, max_blocks, block_size, num_splits, &need);
+  if (ws != MLA_OK) return ws;
+  if (need > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+  void* ptr = device_scratch();
+  if (!ptr) return MLA_ERR_HIP;
+  return decode_impl(dims, scale, batch, t_q, q_abs, kv_cache, dt, num_blocks, block_size, block_table, max_blocks,
+                     seq_lens, 1, 0, 1, out_lat, out_dt, lse, ptr, kNoAllocScratchBytes, num_splits, stream);
 }
 
 mla_status mla_decode_attention_dcp(const mla_dims* dims, float scale, int32_t batch, int32_t t_q, const void* q_abs,

@@ -272,3 +272,18 @@ def test_dcp_and_combine_host_validation():
     assert comb(l=None) == B.MLA_ERR_NULL
     assert comb(out=None) == B.MLA_ERR_NULL
     assert comb(n_rows=0, o=None, l=None, out=None) == B.MLA_OK
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch():
+    # The allocation-free entry point's scratch holds 160 MiB; a plan that
+    # needs more is refused before any device work (explicit range count: no
+    # device query).
+    L = mla.lib()
+    dsv3 = (128, 128, 64, 0, 512)
+    sz = ctypes.c_size_t()
+    assert L.mla_decode_workspace_size(dims(dsv3), 64, 1, 2048, 16, 64, ctypes.byref(sz)) == B.MLA_OK
+    assert sz.value > 160 << 20
+    assert L.mla_decode_attention_noalloc(dims(dsv3), 0.07, 64, 1, FAKE, FAKE, B.MLA_BF16, 100000, 16, FAKE, 2048,
+                                          FAKE, FAKE, B.MLA_BF16, None, 64, None) == B.MLA_ERR_WORKSPACE
+    assert L.mla_decode_attention_noalloc(None, 0.07, 64, 1, FAKE, FAKE, B.MLA_BF16, 100000, 16, FAKE, 2048,
+                                          FAKE, FAKE, B.MLA_BF16, None, 64, None) == B.MLA_ERR_NULL
