@@ -46,7 +46,8 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 # and a hash of the sources it was measured on; a figure is reported only
 # while those sources are unchanged.
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["mla_latent_cache_amd/csrc/decode.hip", "mla_latent_cache_amd/csrc/device_common.hpp",
+KERNEL_SOURCES = ["mla_latent_cache_amd/csrc/decode.hip", "mla_latent_cache_amd/csrc/decode_flat.hip",
+                  "mla_latent_cache_amd/csrc/decode_common.hpp", "mla_latent_cache_amd/csrc/device_common.hpp",
                   "mla_latent_cache_amd/csrc/kernels.hpp", "mla_latent_cache_amd/csrc/mla_api.cpp"]
 
 

@@ -13,33 +13,41 @@
 // sequence of T tiles; range g of G covers tiles [g T / G, (g + 1) T / G), so
 // every workgroup streams the same number of tiles whatever the lengths (the
 // sequence is rebuilt on the device from seq_lens by every workgroup: one
-// load and a wave scan per 64 requests).  Each query tile (qt = 64 or 128
-// query rows x heads of one request) has its own G workgroups, placed so that
-// the query tiles of one range share an XCD and read the cache through one L2.
+// load and a wave scan per 64 requests).  Each query tile (qt = 128 query
+// rows x heads of one request) has its own G workgroups, placed so that the
+// query tiles of one range share an XCD and read the cache through one L2.
 // A request inside one range is finished there (final output and LSE);
 // a request cut by a range end leaves float32 (o, lse) pieces, at most two per
 // workgroup (its first and its last request), which decode_flat_merge combines:
 //   M = max lse_k, w_k = exp(lse_k - M), o = sum w_k o_k / sum w_k,
 //   lse = M + log sum w_k  (all -inf: zeros and -inf).
 //
-// Workgroup: four waves, one per SIMD; wave w owns query rows
-// [16 QB w, 16 QB (w + 1)) of the tile over the full row width, so the scores,
-// the online softmax and the probabilities never leave its registers:
+// Workgroup: four waves, one per SIMD; wave w owns query rows [32 w, 32 w + 32)
+// of the tile (two 16-row blocks) over the full row width, so the scores, the
+// softmax and the probabilities never leave its registers:
 //   * tiles go HBM -> LDS directly (buffer_load ... lds) through a ring of four
 //     tile images, three tiles in flight while one is consumed; one buffer
 //     resource per cache block, sized to the request's valid rows (rows past
 //     the end read as zeros; no address outside a real block is formed);
 //   * S^T = K Q^T with 16x16x32 bf16 MFMA: K as 16-byte LDS reads (one row per
-//     lane), the queries as B operands held in registers for the request;
-//   * online softmax with a delayed maximum (the reference moves only when a
-//     tile's maximum exceeds it by more than kSlack in log2 units);
+//     lane), each read feeding the products of both query blocks; the queries
+//     are B operands held in registers for the request;
+//   * softmax against a fixed reference per row (the maximum of its first
+//     visible tile; later tiles may exceed it by up to kLimit in log2 units,
+//     and a piece that goes further is streamed a second time with its true
+//     maximum), so the output accumulators change only through the matrix
+//     products and stay in the matrix-core registers;
 //   * the probabilities, packed to bf16, are already the B operand of
 //     O^T = V^T P^T (the 16x16 output layout of S^T holds, per lane, the eight
 //     rows that the B operand's eight k-slots take, and the transposing reads
 //     of V^T use the same row order), so P^T stays in registers;
-//   * V^T comes from the same LDS tile with ds_read_b64_tr_b16.
+//   * V^T comes from the same LDS tile with ds_read_b64_tr_b16, each read again
+//     feeding both query blocks.
 // One barrier per tile: after it tile k is resident for every wave and the
-// slot of tile k - 1 is free for tile k + 3.
+// slot of tile k - 1 is free for tile k + 3.  A wave issues one instruction
+// at a time, so the tile step is kept short: per-lane load offsets computed
+// once, 32-bit tile positions, LDS waits two reads at a time, masking only on
+// tiles that reach past a query's horizon.
 #include "decode_common.hpp"
 #include "kernels.hpp"
 
@@ -49,8 +57,12 @@
 namespace mla {
 namespace {
 
-constexpr int kWaves = 8;  // per workgroup, two per SIMD
-constexpr int kRing = 4;   // tile images in LDS
+constexpr int kWaves = 4;   // per workgroup, one per SIMD
+constexpr int kQB = 2;      // 16-row query blocks per wave
+constexpr int kRing = 4;    // tile images in LDS
+constexpr int kKAhead = 6;  // K reads in flight ahead of their products
+constexpr int kVAhead = 4;  // V^T column tiles in flight ahead of their products
+constexpr float kLimit = 64.f;  // log2 headroom of the fixed softmax reference
 
 // LDS image of one 32-row tile (two 16-row cache blocks) of latent rows of
 // width D = 512 + D_ROPE, filled by 1 KB wave-loads (64 lanes x 16 bytes).
@@ -88,31 +100,14 @@ __device__ __forceinline__ void lds_tr_b64(uint32_t addr, uint2& v) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
 }
 template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4& v) {
-  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "i"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait(uint2& x, uint2& y) {
+__device__ __forceinline__ void lgkm_wait(u32x4& x, u32x4& y) {
   static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(x), "+v"(y) : "i"(N) : "memory");
 }
-
-// s_waitcnt vmcnt(n) for the counts the tile ring uses (n = 0 or a multiple
-// of a wave's per-tile load count, at most two tiles).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 16: wait_vmcnt<16>(); break;
-    case 18: wait_vmcnt<18>(); break;
-    case 20: wait_vmcnt<20>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
+template <int N>
+__device__ __forceinline__ void lgkm_wait(uint2& x, uint2& y, uint2& z, uint2& u) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x), "+v"(y), "+v"(z), "+v"(u) : "i"(N) : "memory");
 }
 
 // Tiles of a request of global length Lg (L rows held here), 0 for an empty or
@@ -140,7 +135,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 // is exactly t0 counts as this range's (an empty request belongs to the range
 // holding its position; empty requests at position T belong to the last range).
 struct FlatRange {
-  int64_t T, t0, t1, p_first;
+  int T, t0, t1, p_first;
   int b_first;
 };
 
@@ -156,9 +151,9 @@ __device__ FlatRange flat_range(const FlatArgs& a, int g) {
     }
   }
   FlatRange r;
-  r.T = uniform64(wave_sum64(acc));
-  r.t0 = (int64_t)g * r.T / a.G;
-  r.t1 = (int64_t)(g + 1) * r.T / a.G;
+  r.T = (int)uniform64(wave_sum64(acc));
+  r.t0 = (int)((int64_t)g * r.T / a.G);
+  r.t1 = (int)((int64_t)(g + 1) * r.T / a.G);
   r.b_first = a.batch;
   r.p_first = r.T;
   int64_t run = 0;
@@ -181,7 +176,7 @@ __device__ FlatRange flat_range(const FlatArgs& a, int g) {
     const int cnt = __popcll(__ballot(before));
     if (cnt < 64) {
       r.b_first = __builtin_amdgcn_readfirstlane(base + cnt);
-      r.p_first = uniform64(__shfl(excl, cnt, 64));
+      r.p_first = (int)uniform64(__shfl(excl, cnt, 64));
       break;
     }
     run = __shfl(incl, 63, 64);
@@ -195,9 +190,8 @@ __device__ __forceinline__ int range_of(int64_t t, int64_t T, int G) { return (i
 // A request cursor: request b starts at tile p of the sequence and has n tiles
 // and L rows here.
 struct Cursor {
-  int b;
-  int n;
-  int64_t p, L, Lg;
+  int b, n, p;
+  int64_t L, Lg;
   uint32_t f;
 };
 
@@ -207,18 +201,24 @@ __device__ __forceinline__ void cursor_load(const FlatArgs& a, Cursor& c) {
   c.n = req_tiles(a, c.Lg, c.L, c.f);
 }
 
-// Eight waves (two per SIMD), 128 query rows per workgroup: wave w owns query
-// rows [16 w, 16 w + 16) of the workgroup's query tile over the full row width
-// and all 512 value columns.  A request's 128 query rows x heads share every
-// tile image, so its cache rows go HBM -> LDS once; the two waves on a SIMD
-// cover each other's LDS and matrix-core latencies.
+// Four waves (one per SIMD), 128 query rows per workgroup: wave w owns query
+// rows [32 w, 32 w + 32) of the workgroup's query tile, as two 16-row blocks,
+// over the full row width and all 512 value columns.  A request's 128 query
+// rows x heads share every tile image, so its cache rows go HBM -> LDS once,
+// and every 16-byte K read and every transposing V^T read from LDS feeds two
+// matrix products (one per query block), which halves the LDS read traffic of
+// one-block waves.  The queries (144 registers) and the output accumulators
+// (256) fill most of a SIMD's register file, hence one wave per SIMD: its
+// latencies are covered by reads issued several products ahead.
 template <int D_ROPE>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArgs a) {
   using T = FlatTile<D_ROPE>;
   constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KS = T::KSTEPS;
-  constexpr int QT = 16 * kWaves;  // query rows per workgroup
+  constexpr int QW = 16 * kQB;     // query rows per wave
+  constexpr int QT = QW * kWaves;  // query rows per workgroup
   constexpr int NCT = 32;          // 16-column output tiles of the 512 value columns
   __shared__ __attribute__((aligned(16))) u32x4 ring[kRing * T::IMG];
+  __shared__ int vote[kWaves];
 
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.header[0] = kWorkspaceMagic;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const FlatRange R = flat_range(a, g);
-  const int64_t t0 = R.t0, t1 = R.t1;
+  const int t0 = R.t0, t1 = R.t1;
   const bool last_range = g == a.G - 1;
   if (t0 == t1 && !last_range) {
     // No tiles and no request here; the merge may still walk over this range
@@ -253,86 +253,84 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
   const const_i32* bt_s = (const const_i32*)a.bt;
   const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
 
-  // Tile loads: wave w issues the 1 KB wave-loads u = w + 8 j of a tile image;
-  // load u covers chunk slots [64 u, 64 u + 64), i.e. block u / BLK_LOADS.
-  constexpr int LJ = (T::TILE_LOADS + kWaves - 1) / kWaves;
-  const int c_w = (T::TILE_LOADS - w + kWaves - 1) / kWaves;  // this wave's loads per tile
-  // Global byte offset (within its block) of this lane's 16 bytes of load u;
-  // padding slots get an offset past any block (they read zeros).
-  auto voff = [&](int u) {
-    // Recomputed at every use from an opaque copy of the lane index, so that
-    // the compiler does not hoist the offsets out of the tile loop (they do
-    // not fit in registers next to the queries and accumulators).
-    int ln;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+  // Tile loads: wave w issues the 1 KB wave-loads u = w + kWaves j of a tile
+  // image; load u covers chunk slots [64 u, 64 u + 64), i.e. block u / BLK_LOADS.
+  // vo[j]: global byte offset (within its block) of this lane's 16 bytes of
+  // load j; padding slots get an offset past any block (they read zeros).
+  constexpr int LJ = T::TILE_LOADS / kWaves;  // loads per wave per tile
+  static_assert(T::TILE_LOADS % kWaves == 0, "whole loads per wave");
+  uint32_t vo[LJ];
+#pragma unroll
+  for (int j = 0; j < LJ; ++j) {
+    const int u = w + kWaves * j;
     const int hb = u / T::BLK_LOADS;
-    const int pos = (u - hb * T::BLK_LOADS) * 64 + ln;
+    const int pos = (u - hb * T::BLK_LOADS) * 64 + lane;
     const int rl = pos / STRIDE;
     const int c = (pos - rl * STRIDE) ^ (rl & 7);
-    return c < CH ? (uint32_t)(rl * D + c * 8) * 2u : 0x7ffffff0u;
-  };
+    vo[j] = c < CH ? (uint32_t)(rl * D + c * 8) * 2u : 0x7ffffff0u;
+  }
   const uint32_t ring_base = lds_addr(ring);
 
-  // Producer: the tile loads of tile k go out in two steps.  fetch(k) finds
-  // the request holding tile k and issues the scalar loads of its two block
-  // ids; it runs at the end of a tile step, so the loads complete under the
-  // next step's waits.  launch(k) forms one buffer resource per block (sized
-  // to the request's valid rows) and the tile's ring slot, and records in
-  // slot_bad whether a block id of the tile was outside the cache; the next
-  // S step then issues this wave's 1 KB loads one at a time (dma_part), so
-  // that the memory pipeline takes them while the matrix cores work.
+  // Producer: fetch(k) finds the request holding tile k, issues the scalar
+  // loads of its two block ids and notes how many rows of each block are
+  // valid; it runs one tile step ahead of launch(k), which forms one buffer
+  // resource per block (sized to its valid rows), picks the tile's ring slot
+  // and records in slot_bad whether a block id of the tile was outside the
+  // cache.  The S step then issues this wave's 1 KB loads one at a time
+  // (dma_part), so that the memory pipeline takes them while the matrix
+  // cores work.
   Cursor prod;
   prod.b = R.b_first;
   prod.p = R.p_first;
   if (prod.b < a.batch) cursor_load(a, prod);
   int32_t pid[2] = {-1, -1};
-  int pkl = 0;
+  int pnv[2] = {0, 0};
   uint32_t slot_bad = 0;
-  auto fetch = [&](int64_t k) {
+  auto fetch = [&](int k) {
     while (k >= prod.p + prod.n) {  // k < T, so a request holding it follows
       prod.p += prod.n;
       ++prod.b;
       cursor_load(a, prod);
     }
-    pkl = (int)(k - prod.p);
-    const int nblk = (int)((prod.L + 15) >> 4);
-    const const_i32* row = bt_s + (int64_t)prod.b * a.max_blocks;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) pid[hb] = 2 * pkl + hb < nblk ? row[2 * pkl + hb] : -1;
+    const int pkl = k - prod.p;
+    const int64_t left = prod.L - 32 * (int64_t)pkl;  // rows of the request from this tile on (> 0)
+    const const_i32* row = bt_s + (int64_t)prod.b * a.max_blocks + 2 * pkl;
+    pid[0] = row[0];
+    pnv[0] = left >= 16 ? 16 : (int)left;
+    pnv[1] = left >= 32 ? 16 : (left > 16 ? (int)left - 16 : 0);
+    pid[1] = pnv[1] > 0 ? row[1] : -1;
   };
   i32x4 lrs[2];
   uint32_t lbase = 0;
   auto dma_part = [&](int j) {
     const int u = w + kWaves * j;
-    const bool in_tile = kWaves * j + kWaves - 1 < T::TILE_LOADS || u < T::TILE_LOADS;
     const bool blk0 = kWaves * j + kWaves - 1 < T::BLK_LOADS || (kWaves * j < T::BLK_LOADS && u < T::BLK_LOADS);
-    if (in_tile) dma16(blk0 ? lrs[0] : lrs[1], lbase + (uint32_t)u * 1024u, voff(u));
+    dma16(blk0 ? lrs[0] : lrs[1], lbase + (uint32_t)u * 1024u, vo[j]);
   };
-  auto launch = [&](int64_t k) {
+  auto launch = [&](int k) {
     uint32_t badbit = 0;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int64_t left = prod.L - (int64_t)(2 * pkl + hb) * 16;
-      const int nvalid = left <= 0 ? 0 : (left >= 16 ? 16 : (int)left);
       const bool ok = (uint32_t)pid[hb] < nb32;
-      if (nvalid > 0 && !ok) badbit = 1u;
-      lrs[hb] = raw_rsrc(kv + (int64_t)(ok ? pid[hb] : 0) * (16 * D), ok ? (uint32_t)(nvalid * D * 2) : 0u);
+      if (pnv[hb] > 0 && !ok) badbit = 1u;
+      lrs[hb] = raw_rsrc(kv + (int64_t)(ok ? pid[hb] : 0) * (16 * D), ok ? (uint32_t)(pnv[hb] * D * 2) : 0u);
     }
-    const uint32_t slot = (uint32_t)((k - t0) & (kRing - 1));
+    const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
     slot_bad = (slot_bad & ~(1u << slot)) | (badbit << slot);
     lbase = ring_base + slot * (uint32_t)(T::IMG * 16);
   };
-
-  // First three tiles in flight before anything else; the block ids of the
-  // fourth fetched for the first tile step.
-  int64_t k_next = t0;
-  for (int s = 0; s < kRing - 1 && k_next < t1; ++s) {
-    fetch(k_next);
-    launch(k_next++);
+  // The first kRing - 1 tiles in flight, and the block ids of the next.
+  int k_next = t0;
+  auto prologue = [&]() {
+    for (int s = 0; s < kRing - 1 && k_next < t1; ++s) {
+      fetch(k_next);
+      launch(k_next++);
 #pragma unroll
-    for (int j = 0; j < LJ; ++j) dma_part(j);
-  }
-  if (k_next < t1) fetch(k_next);
+      for (int j = 0; j < LJ; ++j) dma_part(j);
+    }
+    if (k_next < t1) fetch(k_next);
+  };
+  prologue();
 
   // Per-lane LDS offsets within a tile image.  The swizzle only permutes
   // chunks within aligned groups of 8 (128 bytes), so a lane's offset depends
@@ -351,40 +349,52 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
 
   const float sl2 = a.scale * kLog2e;
   uint32_t wflags = 0;
-  const int ql = 16 * w + l16;   // this lane's query row within the workgroup's tile
-  const int qr = mt * QT + ql;   // and within the request
-  const bool q_ok = qr < a.n_q;
+  // This lane's query row of block qb, within the workgroup's tile and within
+  // the request.
+  int ql[kQB], qr[kQB];
+  bool q_ok[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    ql[qb] = QW * w + 16 * qb + l16;
+    qr[qb] = mt * QT + ql[qb];
+    q_ok[qb] = qr[qb] < a.n_q;
+  }
 
-  bf16x8 qf[KS];
-  f32x4 acc[NCT];
+  bf16x8 qf[kQB][KS];
+  f32x4 acc[kQB][NCT];
 
-  // Writes the lane's query row of request b: the value columns (acc times
+  // Writes the lane's query rows of request b: the value columns (acc times
   // inv, or fill_v everywhere) and the LSE, to the final output or to partial
   // slot `pidx` (-1: final).
-  auto write_row = [&](int b, float inv, float lse_v, bool fill, float fill_v, int64_t pidx) {
-    if (!q_ok) return;
-    if (pidx < 0) {
-      const int64_t orow = (int64_t)b * a.n_q + qr;
-      if (a.out_bf16) {
-        uint16_t* o = static_cast<uint16_t*>(a.out) + orow * 512 + 4 * g4;
+  auto write_rows = [&](int b, const float* inv, const float* lse_v, bool fill, float fill_v, int64_t pidx) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const f32x4 v = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[ct] * inv;
-          *reinterpret_cast<uint2*>(o + 16 * ct) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    for (int qb = 0; qb < kQB; ++qb) {
+      if (!q_ok[qb]) continue;
+      if (pidx < 0) {
+        const int64_t orow = (int64_t)b * a.n_q + qr[qb];
+        if (a.out_bf16) {
+          uint16_t* o = static_cast<uint16_t*>(a.out) + orow * 512 + 4 * g4;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 v = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[qb][ct] * inv[qb];
+            *reinterpret_cast<uint2*>(o + 16 * ct) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+        } else {
+          float* o = static_cast<float*>(a.out) + orow * 512 + 4 * g4;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            *reinterpret_cast<f32x4*>(o + 16 * ct) =
+                fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[qb][ct] * inv[qb];
         }
+        if (g4 == 0 && a.lse) a.lse[orow] = lse_v[qb];
       } else {
-        float* o = static_cast<float*>(a.out) + orow * 512 + 4 * g4;
+        float* o = a.o_part + (pidx * QT + ql[qb]) * 512 + 4 * g4;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-          *reinterpret_cast<f32x4*>(o + 16 * ct) = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[ct] * inv;
+          *reinterpret_cast<f32x4*>(o + 16 * ct) =
+              fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[qb][ct] * inv[qb];
+        if (g4 == 0) a.lse_part[pidx * QT + ql[qb]] = lse_v[qb];
       }
-      if (g4 == 0 && a.lse) a.lse[orow] = lse_v;
-    } else {
-      float* o = a.o_part + (pidx * QT + ql) * 512 + 4 * g4;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        *reinterpret_cast<f32x4*>(o + 16 * ct) = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[ct] * inv;
-      if (g4 == 0) a.lse_part[pidx * QT + ql] = lse_v;
     }
   };
 
@@ -396,13 +406,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
     if (cons.p >= t1 && !last_range) break;
     const int b = cons.b;
     if (cons.n == 0) {  // empty or invalid request, owned by this range
-      write_row(b, 0.f, cons.f ? NAN : -INFINITY, true, cons.f ? NAN : 0.f, -1);
+      const float lse_e = cons.f ? NAN : -INFINITY;
+      const float lse2[2] = {lse_e, lse_e};
+      write_rows(b, lse2, lse2, true, cons.f ? NAN : 0.f, -1);
       wflags |= cons.f;
       if (mt == 0 && tid == 0) *reinterpret_cast<i32x4*>(a.req + 4 * (int64_t)b) = i32x4{-1, -1, 0, 0};
       continue;
     }
-    const int64_t ka = cons.p > t0 ? cons.p : t0;
-    const int64_t ke = cons.p + cons.n < t1 ? cons.p + cons.n : t1;
+    const int ka = cons.p > t0 ? cons.p : t0;
+    const int ke = cons.p + cons.n < t1 ? cons.p + cons.n : t1;
     const bool first_piece = ka == cons.p;
     const bool whole = first_piece && ke == cons.p + cons.n;
     if (first_piece && mt == 0 && tid == 0) {
@@ -410,143 +422,235 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
       *reinterpret_cast<i32x4*>(a.req + 4 * (int64_t)b) = i32x4{g, g1, cons.p == t0 ? 0 : 1, 0};
     }
 
-    // The lane's query as B operands of S^T: lane (l16, g4) holds columns
-    // 32 ks + 8 g4 .. + 7 of query row ql; rows past n_q are zero.
-    {
-      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
-                                                         ((int64_t)b * a.n_q + (q_ok ? qr : 0)) * D + 8 * g4);
+    // The lane's queries as B operands of S^T: lane (l16, g4) holds columns
+    // 32 ks + 8 g4 .. + 7 of query rows ql[qb]; rows past n_q are zero.
+    // Rows of this request visible to each query (its causal horizon), and
+    // the fewest any of the wave's valid rows sees: tiles below that need no
+    // mask.
+    int hz[kQB];
+    int hz_min = INT32_MAX;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(q_ok ? src[4 * ks] : u32x4{0u, 0u, 0u, 0u});
+    for (int qb = 0; qb < kQB; ++qb) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
+                                                         ((int64_t)b * a.n_q + (q_ok[qb] ? qr[qb] : 0)) * D + 8 * g4);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = as_bf16x8(q_ok[qb] ? src[4 * ks] : u32x4{0u, 0u, 0u, 0u});
+      const int64_t h = q_ok[qb] ? held_rows(cons.Lg - a.t_q + qr[qb] / a.n_head + 1, a.dcp_world, a.dcp_rank,
+                                             a.dcp_interleave)
+                                 : 0;
+      hz[qb] = (int)(h < cons.L ? h : cons.L);
+      if (q_ok[qb]) hz_min = hz[qb] < hz_min ? hz[qb] : hz_min;
     }
-    // Rows of this request visible to the lane's query (its causal horizon).
-    int hz;
-    {
-      const int64_t h = q_ok ? held_rows(cons.Lg - a.t_q + qr / a.n_head + 1, a.dcp_world, a.dcp_rank,
-                                         a.dcp_interleave)
-                             : 0;
-      hz = (int)(h < cons.L ? h : cons.L);
+    for (int off = 32; off > 0; off >>= 1) {
+      const int o = __shfl_xor(hz_min, off, 64);
+      hz_min = o < hz_min ? o : hz_min;
     }
+    hz_min = __builtin_amdgcn_readfirstlane(hz_min);
     // The query loads are the only vector-memory loads the compiler tracks in
     // this loop: wait for them here (with every tile load issued so far), so it
     // does not put a full wait before every tile's first product.
     wait_vmcnt<0>();
+
+    // Softmax with a fixed reference per pass (log2 units): m_ref is the
+    // maximum of the first tile with a visible row, and later tiles may exceed
+    // it by up to kLimit (probabilities up to 2^kLimit: bf16 and float32 share
+    // the exponent range, so nothing overflows and relative precision is
+    // unchanged).  The accumulators are then touched by the matrix products
+    // alone.  If a tile goes past the limit, the workgroup streams the piece a
+    // second time with the piece's true maximum as the reference.
+    float m_ref[kQB], m_hi[kQB], lsum[kQB];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m2 = -INFINITY, lsum = 0.f;  // softmax state (log2 units)
+    for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = m_hi[qb] = -INFINITY;
     bool bad = false;
-
-    for (int64_t k = ka; k < ke; ++k) {
-      // Tile k resident: this wave's loads of it are done once at most the
-      // loads of the tiles issued after it (k + 1, k + 2) are outstanding (the
-      // first tile of a request was waited for with the query loads).
-      if (k != ka) wait_vm(c_w * ((k + 1 < t1 ? 1 : 0) + (k + 2 < t1 ? 1 : 0)));
-      barrier_keep_loads();  // tile k visible to all waves; tile k - 1 no longer read
-      const bool loading = k_next < t1;
-      if (loading) launch(k_next++);
-      const int kl = (int)(k - cons.p);
-      const uint32_t slot = (uint32_t)((k - t0) & (kRing - 1));
-      if ((slot_bad >> slot) & 1u) bad = true;
-      const uint32_t img = ring_base + slot * (uint32_t)(T::IMG * 16);
-
-      // S^T of the tile: (k-step, block) pairs I = 2 ks + rb, K reads issued
-      // kAhead pairs ahead of their products; this wave's loads of tile k + 3
-      // go out among them.
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      {
-        constexpr int NP = 2 * KS;
-        constexpr int kAhead = 4;
-        // Pair I: k-step ks = I / 2, block rb = I % 2; 128-byte group ks / 2.
-        const uint32_t kaddr[2] = {img + k_off[0], img + k_off[1]};
-        u32x4 kr[NP];
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-          (lds_b128<(I % 2) * T::BLK_POS * 16 + 128 * (I / 4)>(kaddr[(I / 2) % 2], kr[I]), ...);
-        }(std::make_integer_sequence<int, kAhead>{});
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-          (([&] {
-             constexpr int issued = I + kAhead < NP ? I + kAhead : NP;
-             lgkm_wait<issued - 1 - I>(kr[I]);
-             sacc[I % 2] = mfma16x16x32(as_bf16x8(kr[I]), qf[I / 2], sacc[I % 2]);
-             if constexpr (I + kAhead < NP) {
-               constexpr int P = I + kAhead;
-               lds_b128<(P % 2) * T::BLK_POS * 16 + 128 * (P / 4)>(kaddr[(P / 2) % 2], kr[P]);
-             }
-             if constexpr (I % 3 == 1 && I / 3 < LJ) {
-               if (loading) dma_part(I / 3);
-             }
-             __builtin_amdgcn_sched_barrier(0);
-           }()),
-           ...);
-        }(std::make_integer_sequence<int, NP>{});
+    for (int pass = 0;; ++pass) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        lsum[qb] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[qb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      bool over = false;
 
-      // Online softmax of the lane's query over tile rows 16 rb + 4 g4 + i (the
-      // other twelve rows of each block sit in the lanes l16 + 16 g', g' != g4),
-      // and P^T as the B operand of O^T.
-      float sc[8];
-      float tmax = -INFINITY;
-      const int rbase = 32 * kl + 4 * g4;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = rbase + 16 * rb + i < hz ? sacc[rb][i] * sl2 : -INFINITY;
-          sc[4 * rb + i] = v;
-          tmax = fmaxf(tmax, v);
+      for (int k = ka; k < ke; ++k) {
+        // Tile k resident: this wave's loads of it are done once at most the
+        // loads of the tiles issued after it (k + 1, k + 2) are outstanding
+        // (the first tile of a pass was waited for before the loop).
+        if (k != ka) {
+          if (k + 2 < t1)
+            wait_vmcnt<2 * LJ>();
+          else if (k + 1 < t1)
+            wait_vmcnt<LJ>();
+          else
+            wait_vmcnt<0>();
         }
-      tmax = max4rows(tmax);
-      const bool grow = tmax > m2 + kSlack;
-      const float alpha = grow && m2 > -INFINITY ? __builtin_amdgcn_exp2f(m2 - tmax) : 1.f;
-      if (grow) m2 = tmax;
-      const float m_use = m2 == -INFINITY ? 0.f : m2;
-      float pr[8];
+        barrier_keep_loads();  // tile k visible to all waves; tile k - 1 no longer read
+        const bool loading = k_next < t1;
+        if (loading) launch(k_next++);
+        if (k_next < t1) fetch(k_next);  // block ids of the tile the next step issues
+        const int kl = k - cons.p;
+        const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
+        if ((slot_bad >> slot) & 1u) bad = true;
+        const uint32_t img = ring_base + slot * (uint32_t)(T::IMG * 16);
+
+        // S^T of the tile: (k-step, block) pairs I = 2 ks + rb, each K read
+        // feeding both query blocks, read kAhead pairs ahead of their products
+        // and waited for two at a time; this wave's loads of tile k + 3 go
+        // out among them.
+        f32x4 sacc[kQB][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
-      lsum = lsum * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-      const bf16x8 pB = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                        pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
-      if (__ballot(alpha != 1.f)) {
+        for (int qb = 0; qb < kQB; ++qb) sacc[qb][0] = sacc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+          constexpr int NP = 2 * KS;
+          constexpr int kAhead = kKAhead;
+          constexpr int DSTEP = NP / 2 / LJ;  // steps between two tile loads
+          static_assert(kAhead % 2 == 0 && NP % 2 == 0, "reads in pairs");
+          static_assert(DSTEP >= 1 && LJ * DSTEP <= NP / 2, "tile loads spread over the steps");
+          // Pair I: k-step ks = I / 2, block rb = I % 2; 128-byte group ks / 2.
+          const uint32_t kaddr[2] = {img + k_off[0], img + k_off[1]};
+          u32x4 kr[NP];
+          [&]<int... I>(std::integer_sequence<int, I...>) {
+            (lds_b128<(I % 2) * T::BLK_POS * 16 + 128 * (I / 4)>(kaddr[(I / 2) % 2], kr[I]), ...);
+          }(std::make_integer_sequence<int, kAhead>{});
+          [&]<int... J>(std::integer_sequence<int, J...>) {
+            (([&] {
+               constexpr int I = 2 * J;
+               constexpr int issued = I + kAhead < NP ? I + kAhead : NP;
+               lgkm_wait<issued - 2 - I>(kr[I], kr[I + 1]);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[ct] *= alpha;
+               for (int e = 0; e < 2; ++e) {
+                 const bf16x8 kA = as_bf16x8(kr[I + e]);
+#pragma unroll
+                 for (int qb = 0; qb < kQB; ++qb)
+                   sacc[qb][(I + e) % 2] = mfma16x16x32(kA, qf[qb][(I + e) / 2], sacc[qb][(I + e) % 2]);
+               }
+               if constexpr (I + kAhead < NP) {
+                 constexpr int P = I + kAhead;
+                 lds_b128<(P % 2) * T::BLK_POS * 16 + 128 * (P / 4)>(kaddr[(P / 2) % 2], kr[P]);
+                 lds_b128<((P + 1) % 2) * T::BLK_POS * 16 + 128 * ((P + 1) / 4)>(kaddr[((P + 1) / 2) % 2], kr[P + 1]);
+               }
+               if constexpr (J % DSTEP == DSTEP / 2 && J / DSTEP < LJ) {
+                 if (loading) dma_part(J / DSTEP);
+               }
+               __builtin_amdgcn_sched_barrier(0);
+             }()),
+             ...);
+          }(std::make_integer_sequence<int, NP / 2>{});
+        }
+
+        // Softmax of the lane's queries over tile rows 16 rb + 4 g4 + i (the
+        // other twelve rows of each block sit in the lanes l16 + 16 g',
+        // g' != g4), and P^T as the B operand of O^T.  Rows past a query's
+        // horizon are masked, on the tiles that reach past the wave's
+        // smallest horizon only.
+        if (32 * kl + 32 > hz_min) {
+          const int rbase = 32 * kl + 4 * g4;
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (rbase + 16 * rb + i >= hz[qb]) sacc[qb][rb][i] = -INFINITY;
+        }
+        bf16x8 pB[kQB];
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          float tmax = fmaxf(fmaxf(fmaxf(sacc[qb][0][0], sacc[qb][0][1]), fmaxf(sacc[qb][0][2], sacc[qb][0][3])),
+                             fmaxf(fmaxf(sacc[qb][1][0], sacc[qb][1][1]), fmaxf(sacc[qb][1][2], sacc[qb][1][3])));
+          tmax = max4rows(tmax) * sl2;
+          m_hi[qb] = fmaxf(m_hi[qb], tmax);
+          if (m_ref[qb] == -INFINITY) m_ref[qb] = tmax;
+          over |= tmax > m_ref[qb] + kLimit;
+          const float nm = m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb];
+          float pr[8];
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[4 * rb + i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][rb][i], sl2, nm));
+          lsum[qb] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+          pB[qb] = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                   pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+        }
+
+        // O^T += V^T P^T, V^T read kAhead column tiles ahead and waited for two
+        // column tiles at a time, each read feeding both query blocks.
+        {
+          constexpr int kAhead = kVAhead;
+          static_assert(kAhead % 2 == 0, "column tiles in pairs");
+          // Column tile ct: 128-byte group ct / 4, lane offset v_off[ct % 4].
+          const uint32_t vaddr[4] = {img + v_off[0], img + v_off[1], img + v_off[2], img + v_off[3]};
+          uint2 vr[NCT][2];
+          [&]<int... I>(std::integer_sequence<int, I...>) {
+            ((lds_tr_b64<128 * (I / 4)>(vaddr[I % 4], vr[I][0]),
+              lds_tr_b64<T::BLK_POS * 16 + 128 * (I / 4)>(vaddr[I % 4], vr[I][1])),
+             ...);
+          }(std::make_integer_sequence<int, kAhead>{});
+          [&]<int... J>(std::integer_sequence<int, J...>) {
+            (([&] {
+               constexpr int I = 2 * J;
+               constexpr int issued = I + kAhead < NCT ? I + kAhead : NCT;
+               lgkm_wait<2 * (issued - 2 - I)>(vr[I][0], vr[I][1], vr[I + 1][0], vr[I + 1][1]);
+#pragma unroll
+               for (int e = 0; e < 2; ++e) {
+                 const bf16x8 vA = as_bf16x8(u32x4{vr[I + e][0].x, vr[I + e][0].y, vr[I + e][1].x, vr[I + e][1].y});
+#pragma unroll
+                 for (int qb = 0; qb < kQB; ++qb) acc[qb][I + e] = mfma16x16x32(vA, pB[qb], acc[qb][I + e]);
+               }
+               if constexpr (I + kAhead < NCT) {
+                 constexpr int P = I + kAhead;
+                 lds_tr_b64<128 * (P / 4)>(vaddr[P % 4], vr[P][0]);
+                 lds_tr_b64<T::BLK_POS * 16 + 128 * (P / 4)>(vaddr[P % 4], vr[P][1]);
+                 lds_tr_b64<128 * ((P + 1) / 4)>(vaddr[(P + 1) % 4], vr[P + 1][0]);
+                 lds_tr_b64<T::BLK_POS * 16 + 128 * ((P + 1) / 4)>(vaddr[(P + 1) % 4], vr[P + 1][1]);
+               }
+               __builtin_amdgcn_sched_barrier(0);
+             }()),
+             ...);
+          }(std::make_integer_sequence<int, NCT / 2>{});
+        }
       }
 
-      // O^T += V^T P^T, V^T read kAhead column tiles ahead.
-      {
-        constexpr int kAhead = 3;
-        // Column tile ct: 128-byte group ct / 4, lane offset v_off[ct % 4].
-        const uint32_t vaddr[4] = {img + v_off[0], img + v_off[1], img + v_off[2], img + v_off[3]};
-        uint2 vr[NCT][2];
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-          ((lds_tr_b64<128 * (I / 4)>(vaddr[I % 4], vr[I][0]),
-            lds_tr_b64<T::BLK_POS * 16 + 128 * (I / 4)>(vaddr[I % 4], vr[I][1])),
-           ...);
-        }(std::make_integer_sequence<int, kAhead>{});
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-          (([&] {
-             constexpr int issued = I + kAhead < NCT ? I + kAhead : NCT;
-             lgkm_wait<2 * (issued - 1 - I)>(vr[I][0], vr[I][1]);
-             const bf16x8 vA = as_bf16x8(u32x4{vr[I][0].x, vr[I][0].y, vr[I][1].x, vr[I][1].y});
-             acc[I] = mfma16x16x32(vA, pB, acc[I]);
-             if constexpr (I + kAhead < NCT) {
-               constexpr int P = I + kAhead;
-               lds_tr_b64<128 * (P / 4)>(vaddr[P % 4], vr[P][0]);
-               lds_tr_b64<T::BLK_POS * 16 + 128 * (P / 4)>(vaddr[P % 4], vr[P][1]);
-             }
-             __builtin_amdgcn_sched_barrier(0);
-           }()),
-           ...);
-        }(std::make_integer_sequence<int, NCT>{});
-      }
-      if (k_next < t1) fetch(k_next);  // block ids of the tile the next step issues
+      // Every wave votes; a second pass if any query row of the workgroup
+      // needs one (the tile loads are shared, so all waves go again).
+      if (pass > 0) break;
+      if (lane == 0) vote[w] = __ballot(over) != 0 ? 1 : 0;
+      barrier_keep_loads();
+      int redo = 0;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) redo |= vote[i];
+      if (!redo) break;
+      // Rewind the producer to the piece's first tile: drain the loads in
+      // flight, wait until no wave reads the ring, and issue the first tiles
+      // again; the second pass uses each row's maximum over the piece.
+      wait_vmcnt<0>();
+      barrier_keep_loads();
+      prod.b = cons.b;
+      prod.p = cons.p;
+      cursor_load(a, prod);
+      k_next = ka;
+      prologue();
+      if (ka + 2 < t1)
+        wait_vmcnt<2 * LJ>();
+      else if (ka + 1 < t1)
+        wait_vmcnt<LJ>();
+      else
+        wait_vmcnt<0>();
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = m_hi[qb];
     }
 
-    // Finish the piece: 1 / l and the LSE of the lane's query (l summed over
-    // its four lanes), then the final output or a partial slot.
-    const float l = sum4rows(lsum);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float lse_v = bad ? NAN : (l > 0.f ? (m2 + __log2f(l)) * kLn2 : -INFINITY);
+    // Finish the piece: 1 / l and the LSE of the lane's queries (l summed over
+    // their four lanes), then the final output or a partial slot.
+    float inv[kQB], lse_v[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float l = sum4rows(lsum[qb]);
+      inv[qb] = l > 0.f ? 1.f / l : 0.f;
+      lse_v[qb] = bad ? NAN : (l > 0.f ? (m_ref[qb] + __log2f(l)) * kLn2 : -INFINITY);
+    }
     if (bad) wflags |= kBadBlock;
     const int64_t pidx = whole ? -1 : ((int64_t)g * a.m_tiles + mt) * 2 + (cons.p <= t0 ? 0 : 1);
-    write_row(b, inv, lse_v, bad, NAN, pidx);
+    write_rows(b, inv, lse_v, bad, NAN, pidx);
     cons.p += cons.n;
   }
   if (tid == 0) a.status[(int64_t)g * a.m_tiles + mt] = wflags;
@@ -679,14 +783,14 @@ FlatPlan flat_plan(int n_head, int d_rope, int batch, int t_q, int max_blocks, i
   // request on, else 64 (four waves); the query tiles of one range share an
   // XCD, so a cache tile is fetched from HBM once and from L2 by the rest.
   p.qb = kWaves;  // waves per workgroup
-  p.qt = 16 * kWaves;
+  p.qt = 16 * kQB * kWaves;
   p.m_tiles = (int)((n_q + p.qt - 1) / p.qt);
   const int64_t G = ranges < 1 ? 1 : ranges;
-  // Device arithmetic: (t + 1) * G with t < T <= batch * ceil(max_blocks / 2)
-  // in 64 bits, and workgroup and slot counts in 32 bits.
+  // Device arithmetic: tile positions t < T <= batch * ceil(max_blocks / 2) in
+  // 32 bits ((t + 1) * G in 64), and workgroup and slot counts in 32 bits.
   const int64_t max_tiles = (int64_t)(batch > 0 ? batch : 1) * ((max_blocks + 1) / 2);
   const int64_t wgs = (G + 7) / 8 * 8 * p.m_tiles;
-  p.ok = G <= (1 << 24) && max_tiles <= ((int64_t)1 << 38) && wgs <= INT32_MAX;
+  p.ok = G <= (1 << 24) && max_tiles <= (int64_t)(INT32_MAX / 2) && wgs <= INT32_MAX;
   if (!p.ok) return p;
   p.G = (int)G;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };

@@ -291,6 +291,29 @@ def test_flat_schedule_split_invariance_and_determinism():
     full_compare(case, run(dc, num_splits=64))
 
 
+def test_score_growth_far_past_the_first_tile_every_element():
+    # The rope columns of late rows of two requests are scaled by 200, so
+    # their scores exceed those of the request's first tile by far more than
+    # the 128-row kernel's fixed softmax reference allows (64 in log2 units):
+    # the pieces holding the jump are streamed a second time with their true
+    # maximum.  A third request grows by 18-41 (no second pass; probabilities
+    # up to 2^41 before normalisation).  The value columns are untouched.
+    # Every element is compared, for range counts that cut the requests at
+    # different places.
+    spec = spec_small("dsv3_growth", "dsv3_ragged", batch=4, fixed_lens=(700, 1000, 33, 257), max_blocks=64,
+                      lengths="fixed", zero_requests=())
+    case = mi.make_case(spec)
+    kv = mi.bf16_bits_to_f32(case.kv)
+    for b, lo, f in ((1, 300, 200.0), (0, 100, 12.0), (3, 200, 200.0)):
+        for j in range(lo, int(case.seq_lens[b])):
+            kv[case.block_table[b, j // 16], j % 16, spec.kv_rank:] *= f
+    case.kv[...] = mi.to_bf16_bits(kv)
+    for k in (1, 3, 0):
+        res = run(DeviceCase(case), num_splits=k)
+        assert res["status"] == 0
+        full_compare(case, res)
+
+
 # --------------------------------------------------------------------------
 # Properties
 # --------------------------------------------------------------------------
