@@ -66,9 +66,19 @@ typedef struct mla_dims {
   int32_t kv_rank;
 } mla_dims;
 
-typedef enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+/* The enums below are 32-bit integers at the boundary.  Callers may pass any
+ * value; the library rejects codes it does not know (MLA_ERR_ARG).  Under C++
+ * they carry int32_t as their underlying type, so every such value is a valid
+ * enum value there too. */
+#ifdef __cplusplus
+#define MLA_ENUM(name) enum name : int32_t
+#else
+#define MLA_ENUM(name) enum name
+#endif
 
-typedef enum mla_status {
+typedef MLA_ENUM(mla_dtype) { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef MLA_ENUM(mla_status) {
   MLA_OK = 0,
   MLA_ERR_NULL = 1,        /* a required pointer is NULL                   */
   MLA_ERR_DIMS = 2,        /* a geometry field is out of range             */
@@ -262,7 +272,7 @@ mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_l
  * weights expect interleaved rope can run NEOX after permuting the rope rows
  * of its projection weights once at load time (mla.rs, norm_to_neox_perm):
  * query-key dot products are unchanged. */
-typedef enum mla_rope_style { MLA_ROPE_NEOX = 0, MLA_ROPE_INTERLEAVED = 1 } mla_rope_style;
+typedef MLA_ENUM(mla_rope_style) { MLA_ROPE_NEOX = 0, MLA_ROPE_INTERLEAVED = 1 } mla_rope_style;
 
 /* Data-error bit of mla_cache_append. */
 #define MLA_DATA_BAD_SLOT 0x10u /* a slot_mapping entry >= num_blocks * block_size */

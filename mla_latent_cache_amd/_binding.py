@@ -13,7 +13,9 @@ import os
 from typing import Optional, Sequence, Union
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla_amd.so")
+# MLA_AMD_LIB names another build of the same library (the host-sanitized
+# build that the sanitizer test loads); by default the in-tree build.
+LIB_PATH = os.environ.get("MLA_AMD_LIB") or os.path.join(_HERE, "libmla_amd.so")
 
 MLA_F32, MLA_BF16 = 0, 1
 MLA_OK, MLA_ERR_NULL, MLA_ERR_DIMS, MLA_ERR_SHAPE = 0, 1, 2, 3

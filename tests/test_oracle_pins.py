@@ -116,6 +116,29 @@ def test_decompress_matches_einsum(dtype):
     np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("t_q,lens", [(1, [9, 0, 33]), (3, [5, 40])])
+def test_attend_absorbed_is_the_composition_of_pinned_stages(dtype, t_q, lens):
+    """The fused absorbed form equals absorb -> latent decode -> decompress,
+    each of which is pinned on its own (einsum, einsum, torch SDPA)."""
+    spec = small_spec((4, 12, 8, 10, 24), t_q, lens, seed=21 + t_q, dtype=dtype)
+    c = mi.make_case(spec)
+    d = dims_of(spec)
+    out_f, o_f, lse_f, bad_f = oracle.attend_absorbed(d, t_q, c.q_nope, c.q_pe, c.w_uk, c.w_uv, paged(c), c.scale)
+    assert bad_f == 0
+    q_abs = oracle.absorb(d, c.q_nope, c.q_pe, c.w_uk).reshape(len(lens), t_q, spec.n_head, spec.D)
+    o, lse, bad = oracle.decode(d, t_q, q_abs, paged(c), c.scale)
+    assert bad == 0
+    n = len(lens) * t_q
+    out = oracle.decompress(d, o.reshape(n, spec.n_head, spec.kv_rank), c.w_uv).reshape(-1, spec.d_v)
+    np.testing.assert_allclose(o_f, o.reshape(o_f.shape), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out_f, out, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(np.isneginf(lse_f), np.isneginf(lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lse_f[fin], lse[fin], rtol=1e-12, atol=1e-13)
+    assert np.abs(out).max() > 1e-3  # not a vacuous comparison
+
+
 # --------------------------------------------------------------------------
 # Decode attention against torch SDPA on logically ordered rows
 # --------------------------------------------------------------------------
