@@ -23,31 +23,32 @@
 //   lse = M + log sum w_k  (all -inf: zeros and -inf).
 //
 // Workgroup: four waves, one per SIMD; wave w owns query rows [32 w, 32 w + 32)
-// of the tile (two 16-row blocks) over the full row width, so the scores, the
-// softmax and the probabilities never leave its registers:
+// of the tile over the full row width, so the scores, the softmax and the
+// probabilities never leave its registers:
 //   * tiles go HBM -> LDS directly (buffer_load ... lds) through a ring of four
 //     tile images, three tiles in flight while one is consumed; one buffer
 //     resource per cache block, sized to the request's valid rows (rows past
 //     the end read as zeros; no address outside a real block is formed);
-//   * S^T = K Q^T with 16x16x32 bf16 MFMA: K as 16-byte LDS reads (one row per
-//     lane), each read feeding the products of both query blocks; the queries
-//     are B operands held in registers for the request;
+//   * S^T = K Q^T with 32x32x16 bf16 MFMA: the 32 tile rows as the A operand
+//     (one 16-byte LDS read per lane and product), the wave's 32 queries as
+//     B operands held in registers for the request;
 //   * softmax against a fixed reference per row (the maximum of its first
 //     visible tile; later tiles may exceed it by up to kLimit in log2 units,
 //     and a piece that goes further is streamed a second time with its true
 //     maximum), so the output accumulators change only through the matrix
 //     products and stay in the matrix-core registers;
 //   * the probabilities, packed to bf16, are already the B operand of
-//     O^T = V^T P^T (the 16x16 output layout of S^T holds, per lane, the eight
-//     rows that the B operand's eight k-slots take, and the transposing reads
-//     of V^T use the same row order), so P^T stays in registers;
-//   * V^T comes from the same LDS tile with ds_read_b64_tr_b16, each read again
-//     feeding both query blocks.
+//     O^T = V^T P^T (the 32x32 output layout of S^T holds, per lane, the rows
+//     that the B operand's k-slots take, and the transposing reads of V^T use
+//     the same row order), so P^T stays in registers;
+//   * V^T comes from the same LDS tile with ds_read_b64_tr_b16, two reads per
+//     16 rows of a 32-column tile.
 // One barrier per tile: after it tile k is resident for every wave and the
 // slot of tile k - 1 is free for tile k + 3.  A wave issues one instruction
 // at a time, so the tile step is kept short: per-lane load offsets computed
-// once, 32-bit tile positions, LDS waits two reads at a time, masking only on
-// tiles that reach past a query's horizon.
+// once, 32-bit tile positions, LDS waits two reads at a time, the producer's
+// scalar work among the first products, masking only on tiles that reach
+// past a query's horizon.
 #include "decode_common.hpp"
 #include "kernels.hpp"
 
@@ -58,21 +59,20 @@ namespace mla {
 namespace {
 
 constexpr int kWaves = 4;   // per workgroup, one per SIMD
-constexpr int kQB = 2;      // 16-row query blocks per wave
 constexpr int kRing = 4;    // tile images in LDS
 constexpr int kKAhead = 6;  // K reads in flight ahead of their products
-constexpr int kVAhead = 4;  // V^T column tiles in flight ahead of their products
+constexpr int kVAhead = 2;  // 32-column V^T tiles in flight ahead of their products
 constexpr float kLimit = 64.f;  // log2 headroom of the fixed softmax reference
 
 // LDS image of one 32-row tile (two 16-row cache blocks) of latent rows of
 // width D = 512 + D_ROPE, filled by 1 KB wave-loads (64 lanes x 16 bytes).
 // Every row takes 72 16-byte chunk slots (1152 bytes: the whole row at
 // D = 576, the row and 8 empty slots at D = 512), and logical chunk c of row r
-// sits in slot c ^ (r & 7).  With this layout the 16-byte K reads (16 rows of
-// one chunk column) and the transposing V^T reads (4 rows x 32 bytes per 16
-// lanes) are both free of bank conflicts on gfx950 (measured with the LDS
-// bank-conflict counter; the pitch-74 layout with swapped chunk pairs that
-// suits 8-byte K reads gives the 16-byte reads two-way conflicts).
+// sits in slot c ^ (r & 7).  The second block's image starts 128 bytes after
+// the end of the first, so that the 16-byte K reads of one product (32 rows,
+// both blocks, one chunk column) and the transposing V^T reads (4 rows x 64
+// bytes per 32 lanes, rows chosen as below) are free of LDS bank conflicts on
+// gfx950 (measured; without the 128-byte gap the K reads conflict two-way).
 template <int D_ROPE>
 struct FlatTile {
   static constexpr int D = 512 + D_ROPE;
@@ -80,11 +80,28 @@ struct FlatTile {
   static constexpr int STRIDE = 72;                // chunk slots per row
   static constexpr int BLK_POS = 16 * STRIDE;      // chunk slots of one block image
   static constexpr int BLK_LOADS = BLK_POS / 64;   // 1 KB wave-loads per block
-  static constexpr int IMG = 2 * BLK_POS;          // one 32-row tile
+  static constexpr int BLK1 = BLK_POS * 16 + 128;  // byte offset of the second block's image
+  static constexpr int IMG_BYTES = BLK1 + BLK_POS * 16;  // one 32-row tile image
   static constexpr int TILE_LOADS = 2 * BLK_LOADS;
-  static constexpr int KSTEPS = D / 32;            // 32-wide k-steps of q.k
-  static_assert(CH <= STRIDE && BLK_POS % 64 == 0 && TILE_LOADS % 4 == 0, "tile geometry");
+  static constexpr int KSTEPS = D / 16;            // 16-wide k-steps of q.k
+  static_assert(CH <= STRIDE && BLK_POS % 64 == 0 && TILE_LOADS % 4 == 0 && IMG_BYTES % 16 == 0, "tile geometry");
 };
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Position within the tile (block * 16 + row) of the tile row that output row
+// i of S^T = K Q^T stands for.  The products see the 32 rows in this order;
+// it makes every group of 4 rows that one transposing V^T read covers
+// {b, b + 1, b + 4, b + 5} (b = 8 e + 2 h), whose 64-byte pieces sit in
+// different LDS banks.  Output element v of the 32x32 product in lane half h
+// is row i = 8 (v / 4) + 4 h + v % 4, i.e. position 8 (v / 4) + 2 h +
+// {0, 1, 4, 5}[v % 4].
+__host__ __device__ constexpr int tile_pos(int i) {
+  return 8 * (i >> 3) + 2 * ((i >> 2) & 1) + ((i & 1) | ((i & 2) << 1));
+}
 
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 
@@ -202,22 +219,21 @@ __device__ __forceinline__ void cursor_load(const FlatArgs& a, Cursor& c) {
 }
 
 // Four waves (one per SIMD), 128 query rows per workgroup: wave w owns query
-// rows [32 w, 32 w + 32) of the workgroup's query tile, as two 16-row blocks,
-// over the full row width and all 512 value columns.  A request's 128 query
-// rows x heads share every tile image, so its cache rows go HBM -> LDS once,
-// and every 16-byte K read and every transposing V^T read from LDS feeds two
-// matrix products (one per query block), which halves the LDS read traffic of
-// one-block waves.  The queries (144 registers) and the output accumulators
-// (256) fill most of a SIMD's register file, hence one wave per SIMD: its
-// latencies are covered by reads issued several products ahead.
+// rows [32 w, 32 w + 32) of the workgroup's query tile over the full row
+// width and all 512 value columns, as the 32 columns of 32x32x16 bf16 matrix
+// products.  A request's 128 query rows x heads share every tile image, so
+// its cache rows go HBM -> LDS once, and every 16-byte K read and every pair
+// of transposing V^T reads from LDS feeds one 32-row product.  The queries
+// (144 registers) and the output accumulators (256) fill most of a SIMD's
+// register file, hence one wave per SIMD: its latencies are covered by reads
+// issued several products ahead.
 template <int D_ROPE>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArgs a) {
   using T = FlatTile<D_ROPE>;
   constexpr int D = T::D, CH = T::CH, STRIDE = T::STRIDE, KS = T::KSTEPS;
-  constexpr int QW = 16 * kQB;     // query rows per wave
-  constexpr int QT = QW * kWaves;  // query rows per workgroup
-  constexpr int NCT = 32;          // 16-column output tiles of the 512 value columns
-  __shared__ __attribute__((aligned(16))) u32x4 ring[kRing * T::IMG];
+  constexpr int QT = 32 * kWaves;  // query rows per workgroup
+  constexpr int NCT = 16;          // 32-column output tiles of the 512 value columns
+  __shared__ __attribute__((aligned(16))) u32x4 ring[kRing * T::IMG_BYTES / 16];
   __shared__ int vote[kWaves];
 
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -235,7 +251,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int j32 = lane & 31, h = lane >> 5;  // query column of the products, lane half
+  const int l16 = lane & 15;
 
   const FlatRange R = flat_range(a, g);
   const int t0 = R.t0, t1 = R.t1;
@@ -254,9 +271,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
   const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
 
   // Tile loads: wave w issues the 1 KB wave-loads u = w + kWaves j of a tile
-  // image; load u covers chunk slots [64 u, 64 u + 64), i.e. block u / BLK_LOADS.
-  // vo[j]: global byte offset (within its block) of this lane's 16 bytes of
-  // load j; padding slots get an offset past any block (they read zeros).
+  // image; load u covers chunk slots [64 u', 64 u' + 64) of block u / BLK_LOADS
+  // (u' = u % BLK_LOADS).  vo[j]: global byte offset (within its block) of this
+  // lane's 16 bytes of load j; padding slots get an offset past any block
+  // (they read zeros).
   constexpr int LJ = T::TILE_LOADS / kWaves;  // loads per wave per tile
   static_assert(T::TILE_LOADS % kWaves == 0, "whole loads per wave");
   uint32_t vo[LJ];
@@ -305,7 +323,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
   auto dma_part = [&](int j) {
     const int u = w + kWaves * j;
     const bool blk0 = kWaves * j + kWaves - 1 < T::BLK_LOADS || (kWaves * j < T::BLK_LOADS && u < T::BLK_LOADS);
-    dma16(blk0 ? lrs[0] : lrs[1], lbase + (uint32_t)u * 1024u, vo[j]);
+    dma16(blk0 ? lrs[0] : lrs[1], lbase + (uint32_t)u * 1024u + (blk0 ? 0u : 128u), vo[j]);
   };
   auto launch = [&](int k) {
     uint32_t badbit = 0;
@@ -317,7 +335,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
     }
     const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
     slot_bad = (slot_bad & ~(1u << slot)) | (badbit << slot);
-    lbase = ring_base + slot * (uint32_t)(T::IMG * 16);
+    lbase = ring_base + slot * (uint32_t)T::IMG_BYTES;
   };
   // The first kRing - 1 tiles in flight, and the block ids of the next.
   int k_next = t0;
@@ -332,69 +350,77 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
   };
   prologue();
 
-  // Per-lane LDS offsets within a tile image.  The swizzle only permutes
-  // chunks within aligned groups of 8 (128 bytes), so a lane's offset depends
-  // on the k-step (column tile) modulo 2 (4) plus a whole number of groups.
-  // K (A operand of S^T), block rb, k-step ks: row l16, chunk 4 ks + g4.
-  uint32_t k_off[2];
+  // Per-lane LDS offsets within a tile image (the swizzle only permutes
+  // chunks within aligned groups of 8, so a lane's offset depends on the
+  // k-step or column tile modulo a small period plus whole groups).
+  // K (A operand of S^T), k-step s: tile row tile_pos(j32), chunk 2 s + h.
+  uint32_t k_off[4];
+  {
+    const int p = tile_pos(j32), r = p & 15;
+    const uint32_t blk = (p >> 4) ? (uint32_t)T::BLK1 : 0u;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) k_off[e] = (uint32_t)((l16 * STRIDE + ((4 * e + g4) ^ (l16 & 7))) * 16);
-  // V^T (A operand of O^T), column tile ct: rows 4 g4 + l16 / 4 of each block,
-  // columns 16 ct + 4 (l16 % 4) .. + 3, i.e. chunk 2 ct + (l16 % 4) / 2.
-  const int rr = 4 * g4 + (l16 >> 2);
-  uint32_t v_off[4];
+    for (int e = 0; e < 4; ++e) k_off[e] = blk + (uint32_t)((r * STRIDE + ((2 * e + h) ^ (r & 7))) * 16);
+  }
+  // V^T (A operand of O^T), 32-column tile ct, rows of read e in block kh:
+  // lane supplies row 8 e + 2 h + {0, 1, 4, 5}[l16 / 4] and the 8 bytes of
+  // columns 32 ct + 16 (j32 / 16) + 4 (l16 % 4) .. + 3, and receives column
+  // 32 ct + j32 of the four rows.
+  uint32_t v_off[2][2];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    v_off[e] = (uint32_t)((rr * STRIDE + ((2 * e + ((l16 & 3) >> 1)) ^ (rr & 7))) * 16 + (l16 & 1) * 8);
+  for (int e = 0; e < 2; ++e) {
+    const int r = 8 * e + 2 * h + (((l16 >> 2) & 1) | (((l16 >> 2) & 2) << 1));
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp) {
+      const int chunk = 4 * cp + 2 * (j32 >> 4) + ((l16 & 3) >> 1);
+      v_off[e][cp] = (uint32_t)((r * STRIDE + (chunk ^ (r & 7))) * 16 + (l16 & 1) * 8);
+    }
+  }
 
   const float sl2 = a.scale * kLog2e;
   uint32_t wflags = 0;
-  // This lane's query row of block qb, within the workgroup's tile and within
-  // the request.
-  int ql[kQB], qr[kQB];
-  bool q_ok[kQB];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    ql[qb] = QW * w + 16 * qb + l16;
-    qr[qb] = mt * QT + ql[qb];
-    q_ok[qb] = qr[qb] < a.n_q;
-  }
+  // This lane's query row, within the workgroup's tile and within the request.
+  const int ql = 32 * w + j32;
+  const int qr = mt * QT + ql;
+  const bool q_ok = qr < a.n_q;
 
-  bf16x8 qf[kQB][KS];
-  f32x4 acc[kQB][NCT];
+  bf16x8 qf[KS];
+  f32x16 acc[NCT];
 
-  // Writes the lane's query rows of request b: the value columns (acc times
-  // inv, or fill_v everywhere) and the LSE, to the final output or to partial
-  // slot `pidx` (-1: final).
-  auto write_rows = [&](int b, const float* inv, const float* lse_v, bool fill, float fill_v, int64_t pidx) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      if (!q_ok[qb]) continue;
-      if (pidx < 0) {
-        const int64_t orow = (int64_t)b * a.n_q + qr[qb];
-        if (a.out_bf16) {
-          uint16_t* o = static_cast<uint16_t*>(a.out) + orow * 512 + 4 * g4;
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 v = fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[qb][ct] * inv[qb];
-            *reinterpret_cast<uint2*>(o + 16 * ct) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          }
-        } else {
-          float* o = static_cast<float*>(a.out) + orow * 512 + 4 * g4;
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-            *reinterpret_cast<f32x4*>(o + 16 * ct) =
-                fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[qb][ct] * inv[qb];
-        }
-        if (g4 == 0 && a.lse) a.lse[orow] = lse_v[qb];
-      } else {
-        float* o = a.o_part + (pidx * QT + ql[qb]) * 512 + 4 * g4;
+  // Writes the lane's query row of request b: its value columns
+  // 32 ct + 8 (v / 4) + 4 h + v % 4 (acc times inv, or fill_v everywhere) and
+  // the LSE, to the final output or to partial slot `pidx` (-1: final).
+  auto write_row = [&](int b, float inv, float lse_v, bool fill, float fill_v, int64_t pidx) {
+    if (!q_ok) return;
+    auto val = [&](int ct, int q) {
+      return fill ? f32x4{fill_v, fill_v, fill_v, fill_v}
+                  : f32x4{acc[ct][4 * q], acc[ct][4 * q + 1], acc[ct][4 * q + 2], acc[ct][4 * q + 3]} * inv;
+    };
+    if (pidx < 0) {
+      const int64_t orow = (int64_t)b * a.n_q + qr;
+      if (a.out_bf16) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + orow * 512 + 4 * h;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-          *reinterpret_cast<f32x4*>(o + 16 * ct) =
-              fill ? f32x4{fill_v, fill_v, fill_v, fill_v} : acc[qb][ct] * inv[qb];
-        if (g4 == 0) a.lse_part[pidx * QT + ql[qb]] = lse_v[qb];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = val(ct, q);
+            *reinterpret_cast<uint2*>(o + 32 * ct + 8 * q) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+      } else {
+        float* o = static_cast<float*>(a.out) + orow * 512 + 4 * h;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * q) = val(ct, q);
       }
+      if (h == 0 && a.lse) a.lse[orow] = lse_v;
+    } else {
+      float* o = a.o_part + (pidx * QT + ql) * 512 + 4 * h;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * q) = val(ct, q);
+      if (h == 0) a.lse_part[pidx * QT + ql] = lse_v;
     }
   };
 
@@ -406,9 +432,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
     if (cons.p >= t1 && !last_range) break;
     const int b = cons.b;
     if (cons.n == 0) {  // empty or invalid request, owned by this range
-      const float lse_e = cons.f ? NAN : -INFINITY;
-      const float lse2[2] = {lse_e, lse_e};
-      write_rows(b, lse2, lse2, true, cons.f ? NAN : 0.f, -1);
+      write_row(b, 0.f, cons.f ? NAN : -INFINITY, true, cons.f ? NAN : 0.f, -1);
       wflags |= cons.f;
       if (mt == 0 && tid == 0) *reinterpret_cast<i32x4*>(a.req + 4 * (int64_t)b) = i32x4{-1, -1, 0, 0};
       continue;
@@ -422,25 +446,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
       *reinterpret_cast<i32x4*>(a.req + 4 * (int64_t)b) = i32x4{g, g1, cons.p == t0 ? 0 : 1, 0};
     }
 
-    // The lane's queries as B operands of S^T: lane (l16, g4) holds columns
-    // 32 ks + 8 g4 .. + 7 of query rows ql[qb]; rows past n_q are zero.
-    // Rows of this request visible to each query (its causal horizon), and
-    // the fewest any of the wave's valid rows sees: tiles below that need no
-    // mask.
-    int hz[kQB];
-    int hz_min = INT32_MAX;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    // The lane's query as B operands of S^T: columns 16 s + 8 h .. + 7 of
+    // query row qr (zero past n_q); the rows of this request visible to it
+    // (its causal horizon), and the fewest any of the wave's valid rows sees:
+    // tiles below that need no mask.
+    {
       const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
-                                                         ((int64_t)b * a.n_q + (q_ok[qb] ? qr[qb] : 0)) * D + 8 * g4);
+                                                         ((int64_t)b * a.n_q + (q_ok ? qr : 0)) * D + 8 * h);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = as_bf16x8(q_ok[qb] ? src[4 * ks] : u32x4{0u, 0u, 0u, 0u});
-      const int64_t h = q_ok[qb] ? held_rows(cons.Lg - a.t_q + qr[qb] / a.n_head + 1, a.dcp_world, a.dcp_rank,
-                                             a.dcp_interleave)
-                                 : 0;
-      hz[qb] = (int)(h < cons.L ? h : cons.L);
-      if (q_ok[qb]) hz_min = hz[qb] < hz_min ? hz[qb] : hz_min;
+      for (int s = 0; s < KS; ++s) qf[s] = as_bf16x8(q_ok ? src[2 * s] : u32x4{0u, 0u, 0u, 0u});
     }
+    int hz;
+    {
+      const int64_t hh = q_ok ? held_rows(cons.Lg - a.t_q + qr / a.n_head + 1, a.dcp_world, a.dcp_rank,
+                                          a.dcp_interleave)
+                              : 0;
+      hz = (int)(hh < cons.L ? hh : cons.L);
+    }
+    int hz_min = q_ok ? hz : INT32_MAX;
     for (int off = 32; off > 0; off >>= 1) {
       const int o = __shfl_xor(hz_min, off, 64);
       hz_min = o < hz_min ? o : hz_min;
@@ -458,17 +481,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
     // unchanged).  The accumulators are then touched by the matrix products
     // alone.  If a tile goes past the limit, the workgroup streams the piece a
     // second time with the piece's true maximum as the reference.
-    float m_ref[kQB], m_hi[kQB], lsum[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = m_hi[qb] = -INFINITY;
+    float m_ref = -INFINITY, m_hi = -INFINITY, lsum = 0.f;
     bool bad = false;
     for (int pass = 0;; ++pass) {
+      lsum = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        lsum[qb] = 0.f;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[qb][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x16{};
       bool over = false;
 
       for (int k = ka; k < ke; ++k) {
@@ -485,48 +503,45 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
         }
         barrier_keep_loads();  // tile k visible to all waves; tile k - 1 no longer read
         const bool loading = k_next < t1;
-        if (loading) launch(k_next++);
-        if (k_next < t1) fetch(k_next);  // block ids of the tile the next step issues
         const int kl = k - cons.p;
         const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
         if ((slot_bad >> slot) & 1u) bad = true;
-        const uint32_t img = ring_base + slot * (uint32_t)(T::IMG * 16);
+        const uint32_t img = ring_base + slot * (uint32_t)T::IMG_BYTES;
 
-        // S^T of the tile: (k-step, block) pairs I = 2 ks + rb, each K read
-        // feeding both query blocks, read kAhead pairs ahead of their products
-        // and waited for two at a time; this wave's loads of tile k + 3 go
-        // out among them.
-        f32x4 sacc[kQB][2];
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) sacc[qb][0] = sacc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // S^T of the tile (32 rows x the wave's 32 queries), one product per
+        // 16-wide k-step s, K read kAhead steps ahead and waited for two at a
+        // time.  The scalar work of the producer runs among the first
+        // products (launch of tile k + 3 in step 0, the block ids of the tile
+        // after it in step 2), and this wave's loads of tile k + 3 go out one
+        // per odd step.
+        f32x16 sacc = {};
         {
-          constexpr int NP = 2 * KS;
           constexpr int kAhead = kKAhead;
-          constexpr int DSTEP = NP / 2 / LJ;  // steps between two tile loads
-          static_assert(kAhead % 2 == 0 && NP % 2 == 0, "reads in pairs");
-          static_assert(DSTEP >= 1 && LJ * DSTEP <= NP / 2, "tile loads spread over the steps");
-          // Pair I: k-step ks = I / 2, block rb = I % 2; 128-byte group ks / 2.
-          const uint32_t kaddr[2] = {img + k_off[0], img + k_off[1]};
-          u32x4 kr[NP];
+          constexpr int DSTEP = KS / 2 / LJ;  // two-read steps between two tile loads
+          static_assert(kAhead % 2 == 0 && KS % 2 == 0 && DSTEP >= 1 && LJ * DSTEP <= KS / 2, "S step plan");
+          // k-step s: chunk 2 s + h, i.e. lane offset k_off[s % 4] plus 128 (s / 4) bytes.
+          const uint32_t kaddr[4] = {img + k_off[0], img + k_off[1], img + k_off[2], img + k_off[3]};
+          u32x4 kr[KS];
           [&]<int... I>(std::integer_sequence<int, I...>) {
-            (lds_b128<(I % 2) * T::BLK_POS * 16 + 128 * (I / 4)>(kaddr[(I / 2) % 2], kr[I]), ...);
+            (lds_b128<128 * (I / 4)>(kaddr[I % 4], kr[I]), ...);
           }(std::make_integer_sequence<int, kAhead>{});
           [&]<int... J>(std::integer_sequence<int, J...>) {
             (([&] {
                constexpr int I = 2 * J;
-               constexpr int issued = I + kAhead < NP ? I + kAhead : NP;
+               constexpr int issued = I + kAhead < KS ? I + kAhead : KS;
                lgkm_wait<issued - 2 - I>(kr[I], kr[I + 1]);
-#pragma unroll
-               for (int e = 0; e < 2; ++e) {
-                 const bf16x8 kA = as_bf16x8(kr[I + e]);
-#pragma unroll
-                 for (int qb = 0; qb < kQB; ++qb)
-                   sacc[qb][(I + e) % 2] = mfma16x16x32(kA, qf[qb][(I + e) / 2], sacc[qb][(I + e) % 2]);
-               }
-               if constexpr (I + kAhead < NP) {
+               sacc = mfma32x32x16(as_bf16x8(kr[I]), qf[I], sacc);
+               sacc = mfma32x32x16(as_bf16x8(kr[I + 1]), qf[I + 1], sacc);
+               if constexpr (I + kAhead < KS) {
                  constexpr int P = I + kAhead;
-                 lds_b128<(P % 2) * T::BLK_POS * 16 + 128 * (P / 4)>(kaddr[(P / 2) % 2], kr[P]);
-                 lds_b128<((P + 1) % 2) * T::BLK_POS * 16 + 128 * ((P + 1) / 4)>(kaddr[((P + 1) / 2) % 2], kr[P + 1]);
+                 lds_b128<128 * (P / 4)>(kaddr[P % 4], kr[P]);
+                 lds_b128<128 * ((P + 1) / 4)>(kaddr[(P + 1) % 4], kr[P + 1]);
+               }
+               if constexpr (J == 0) {
+                 if (loading) launch(k_next++);
+               }
+               if constexpr (J == 2) {
+                 if (k_next < t1) fetch(k_next);  // block ids of the tile the next step issues
                }
                if constexpr (J % DSTEP == DSTEP / 2 && J / DSTEP < LJ) {
                  if (loading) dma_part(J / DSTEP);
@@ -534,79 +549,83 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
                __builtin_amdgcn_sched_barrier(0);
              }()),
              ...);
-          }(std::make_integer_sequence<int, NP / 2>{});
+          }(std::make_integer_sequence<int, KS / 2>{});
         }
 
-        // Softmax of the lane's queries over tile rows 16 rb + 4 g4 + i (the
-        // other twelve rows of each block sit in the lanes l16 + 16 g',
-        // g' != g4), and P^T as the B operand of O^T.  Rows past a query's
-        // horizon are masked, on the tiles that reach past the wave's
-        // smallest horizon only.
+        // Softmax of the lane's query over its 16 tile rows (element v is tile
+        // position 8 (v / 4) + 2 h + {0, 1, 4, 5}[v % 4]; the other 16 rows sit
+        // in lane ^ 32).  Rows past a query's horizon are masked, on the tiles
+        // that reach past the wave's smallest horizon only.
         if (32 * kl + 32 > hz_min) {
-          const int rbase = 32 * kl + 4 * g4;
+          const int base = 32 * kl + 2 * h;
 #pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (rbase + 16 * rb + i >= hz[qb]) sacc[qb][rb][i] = -INFINITY;
+          for (int v = 0; v < 16; ++v)
+            if (base + 8 * (v >> 2) + ((v & 1) | ((v & 2) << 1)) >= hz) sacc[v] = -INFINITY;
         }
-        bf16x8 pB[kQB];
+        bf16x8 pB[2];
+        {
+          float tmax = sacc[0];
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          float tmax = fmaxf(fmaxf(fmaxf(sacc[qb][0][0], sacc[qb][0][1]), fmaxf(sacc[qb][0][2], sacc[qb][0][3])),
-                             fmaxf(fmaxf(sacc[qb][1][0], sacc[qb][1][1]), fmaxf(sacc[qb][1][2], sacc[qb][1][3])));
-          tmax = max4rows(tmax) * sl2;
-          m_hi[qb] = fmaxf(m_hi[qb], tmax);
-          if (m_ref[qb] == -INFINITY) m_ref[qb] = tmax;
-          over |= tmax > m_ref[qb] + kLimit;
-          const float nm = m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb];
-          float pr[8];
+          for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sacc[v]);
+          {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          }
+          tmax *= sl2;
+          m_hi = fmaxf(m_hi, tmax);
+          if (m_ref == -INFINITY) m_ref = tmax;
+          over |= tmax > m_ref + kLimit;
+          const float nm = m_ref == -INFINITY ? 0.f : -m_ref;
+          float pr[16];
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
+          for (int v = 0; v < 16; ++v) pr[v] = __builtin_amdgcn_exp2f(fmaf(sacc[v], sl2, nm));
+          float ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pr[4 * rb + i] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][rb][i], sl2, nm));
-          lsum[qb] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-          pB[qb] = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                   pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+          for (int q = 0; q < 4; ++q) ps += (pr[4 * q] + pr[4 * q + 1]) + (pr[4 * q + 2] + pr[4 * q + 3]);
+          lsum += ps;
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh)
+            pB[kh] = as_bf16x8(u32x4{pack_bf16x2(pr[8 * kh], pr[8 * kh + 1]), pack_bf16x2(pr[8 * kh + 2], pr[8 * kh + 3]),
+                                     pack_bf16x2(pr[8 * kh + 4], pr[8 * kh + 5]), pack_bf16x2(pr[8 * kh + 6], pr[8 * kh + 7])});
         }
 
-        // O^T += V^T P^T, V^T read kAhead column tiles ahead and waited for two
-        // column tiles at a time, each read feeding both query blocks.
+        // O^T += V^T P^T over the two 16-row halves (blocks) of the tile: the
+        // k-slots 8 h + t of half kh are tile positions 16 kh + 8 (t / 4) + 2 h +
+        // {0, 1, 4, 5}[t % 4], the rows of the two transposing reads e = t / 4.
+        // V^T read kAhead column tiles ahead and waited for one column tile
+        // (four reads) at a time.
         {
           constexpr int kAhead = kVAhead;
-          static_assert(kAhead % 2 == 0, "column tiles in pairs");
-          // Column tile ct: 128-byte group ct / 4, lane offset v_off[ct % 4].
-          const uint32_t vaddr[4] = {img + v_off[0], img + v_off[1], img + v_off[2], img + v_off[3]};
-          uint2 vr[NCT][2];
+          uint2 vr[NCT][2][2];  // [ct][kh][e]
+          auto vread = [&]<int CT>(std::integral_constant<int, CT>) {
+            constexpr uint32_t cofs = 128u * (CT / 2);
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+              for (int e = 0; e < 2; ++e) {
+                if (kh == 0)
+                  lds_tr_b64<cofs>(img + v_off[e][CT % 2], vr[CT][kh][e]);
+                else
+                  lds_tr_b64<cofs + T::BLK1>(img + v_off[e][CT % 2], vr[CT][kh][e]);
+              }
+          };
           [&]<int... I>(std::integer_sequence<int, I...>) {
-            ((lds_tr_b64<128 * (I / 4)>(vaddr[I % 4], vr[I][0]),
-              lds_tr_b64<T::BLK_POS * 16 + 128 * (I / 4)>(vaddr[I % 4], vr[I][1])),
-             ...);
+            (vread(std::integral_constant<int, I>{}), ...);
           }(std::make_integer_sequence<int, kAhead>{});
-          [&]<int... J>(std::integer_sequence<int, J...>) {
+          [&]<int... I>(std::integer_sequence<int, I...>) {
             (([&] {
-               constexpr int I = 2 * J;
                constexpr int issued = I + kAhead < NCT ? I + kAhead : NCT;
-               lgkm_wait<2 * (issued - 2 - I)>(vr[I][0], vr[I][1], vr[I + 1][0], vr[I + 1][1]);
+               lgkm_wait<4 * (issued - 1 - I)>(vr[I][0][0], vr[I][0][1], vr[I][1][0], vr[I][1][1]);
 #pragma unroll
-               for (int e = 0; e < 2; ++e) {
-                 const bf16x8 vA = as_bf16x8(u32x4{vr[I + e][0].x, vr[I + e][0].y, vr[I + e][1].x, vr[I + e][1].y});
-#pragma unroll
-                 for (int qb = 0; qb < kQB; ++qb) acc[qb][I + e] = mfma16x16x32(vA, pB[qb], acc[qb][I + e]);
+               for (int kh = 0; kh < 2; ++kh) {
+                 const bf16x8 vA = as_bf16x8(u32x4{vr[I][kh][0].x, vr[I][kh][0].y, vr[I][kh][1].x, vr[I][kh][1].y});
+                 acc[I] = mfma32x32x16(vA, pB[kh], acc[I]);
                }
-               if constexpr (I + kAhead < NCT) {
-                 constexpr int P = I + kAhead;
-                 lds_tr_b64<128 * (P / 4)>(vaddr[P % 4], vr[P][0]);
-                 lds_tr_b64<T::BLK_POS * 16 + 128 * (P / 4)>(vaddr[P % 4], vr[P][1]);
-                 lds_tr_b64<128 * ((P + 1) / 4)>(vaddr[(P + 1) % 4], vr[P + 1][0]);
-                 lds_tr_b64<T::BLK_POS * 16 + 128 * ((P + 1) / 4)>(vaddr[(P + 1) % 4], vr[P + 1][1]);
-               }
+               if constexpr (I + kAhead < NCT) vread(std::integral_constant<int, I + kAhead>{});
                __builtin_amdgcn_sched_barrier(0);
              }()),
              ...);
-          }(std::make_integer_sequence<int, NCT / 2>{});
+          }(std::make_integer_sequence<int, NCT>{});
         }
       }
 
@@ -635,22 +654,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
         wait_vmcnt<LJ>();
       else
         wait_vmcnt<0>();
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) m_ref[qb] = m_hi[qb];
+      m_ref = m_hi;
     }
 
-    // Finish the piece: 1 / l and the LSE of the lane's queries (l summed over
-    // their four lanes), then the final output or a partial slot.
-    float inv[kQB], lse_v[kQB];
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float l = sum4rows(lsum[qb]);
-      inv[qb] = l > 0.f ? 1.f / l : 0.f;
-      lse_v[qb] = bad ? NAN : (l > 0.f ? (m_ref[qb] + __log2f(l)) * kLn2 : -INFINITY);
+    // Finish the piece: 1 / l and the LSE of the lane's query (l summed over
+    // its two lanes), then the final output or a partial slot.
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+      const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float lse_v = bad ? NAN : (l > 0.f ? (m_ref + __log2f(l)) * kLn2 : -INFINITY);
+      if (bad) wflags |= kBadBlock;
+      const int64_t pidx = whole ? -1 : ((int64_t)g * a.m_tiles + mt) * 2 + (cons.p <= t0 ? 0 : 1);
+      write_row(b, inv, lse_v, bad, NAN, pidx);
     }
-    if (bad) wflags |= kBadBlock;
-    const int64_t pidx = whole ? -1 : ((int64_t)g * a.m_tiles + mt) * 2 + (cons.p <= t0 ? 0 : 1);
-    write_rows(b, inv, lse_v, bad, NAN, pidx);
     cons.p += cons.n;
   }
   if (tid == 0) a.status[(int64_t)g * a.m_tiles + mt] = wflags;
@@ -783,7 +800,7 @@ FlatPlan flat_plan(int n_head, int d_rope, int batch, int t_q, int max_blocks, i
   // request on, else 64 (four waves); the query tiles of one range share an
   // XCD, so a cache tile is fetched from HBM once and from L2 by the rest.
   p.qb = kWaves;  // waves per workgroup
-  p.qt = 16 * kQB * kWaves;
+  p.qt = 32 * kWaves;
   p.m_tiles = (int)((n_q + p.qt - 1) / p.qt);
   const int64_t G = ranges < 1 ? 1 : ranges;
   // Device arithmetic: tile positions t < T <= batch * ceil(max_blocks / 2) in
