@@ -17,8 +17,9 @@
 // rows x heads of one request) has its own G workgroups, placed so that the
 // query tiles of one range share an XCD and read the cache through one L2.
 // A request inside one range is finished there (final output and LSE);
-// a request cut by a range end leaves float32 (o, lse) pieces, at most two per
-// workgroup (its first and its last request), which decode_flat_merge combines:
+// a request cut by a range end leaves (o, lse) pieces, at most two per
+// workgroup (its first and its last request; o in the output's type, bf16 or
+// float32, lse in float32), which decode_flat_merge combines:
 //   M = max lse_k, w_k = exp(lse_k - M), o = sum w_k o_k / sum w_k,
 //   lse = M + log sum w_k  (all -inf: zeros and -inf).
 //
@@ -415,11 +416,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
       }
       if (h == 0 && a.lse) a.lse[orow] = lse_v;
     } else {
-      float* o = a.o_part + (pidx * QT + ql) * 512 + 4 * h;
+      // A piece is stored in the output's type: bf16 when the final output is
+      // bf16 (it is rounded to bf16 anyway), else float32.
+      if (a.out_bf16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.o_part) + (pidx * QT + ql) * 512 + 4 * h;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * q) = val(ct, q);
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = val(ct, q);
+            *reinterpret_cast<uint2*>(o + 32 * ct + 8 * q) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+      } else {
+        float* o = a.o_part + (pidx * QT + ql) * 512 + 4 * h;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(o + 32 * ct + 8 * q) = val(ct, q);
+      }
       if (h == 0) a.lse_part[pidx * QT + ql] = lse_v;
     }
   };
@@ -683,6 +697,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
 // ---------------------------------------------------------------------------
 constexpr int kMergeRows = 4;
 
+// Four bf16 values (two packed pairs, low half first) widened to float32.
+__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 v) {
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+               __uint_as_float(v.y & 0xffff0000u)};
+}
+
 __device__ __forceinline__ float wmax(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
@@ -740,8 +760,14 @@ __global__ __launch_bounds__(64 * (W > 1 ? W : kMergeRows)) void decode_flat_mer
         const int kk = k + u < k1 ? k + u : k1 - 1;
         const int64_t base = (pidx(kk) * a.qt + ql) * 512;
         wk[u] = lse_of(kk);
-        x0[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 4 * lane);
-        x1[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 256 + 4 * lane);
+        if (a.out_bf16) {
+          const uint16_t* op = reinterpret_cast<const uint16_t*>(a.o_part) + base;
+          x0[u] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(op + 4 * lane));
+          x1[u] = bf16x4_to_f32(*reinterpret_cast<const uint2*>(op + 256 + 4 * lane));
+        } else {
+          x0[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 4 * lane);
+          x1[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 256 + 4 * lane);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

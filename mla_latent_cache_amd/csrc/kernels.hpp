@@ -62,7 +62,7 @@ struct Plan {
 //   then (256-aligned) int32x4 per request: first and last range holding it,
 //                      partial slot of the first piece
 //   then (256-aligned) lse partials f32 [G][m_tiles][2][qt]
-//   then (256-aligned) o partials   f32 [G][m_tiles][2][qt][512]
+//   then (256-aligned) o partials   [G][m_tiles][2][qt][512], bf16 when the output is bf16, else f32
 struct FlatArgs {
   const void* q;           // [B][t_q][H][D]
   const void* kv;          // [num_blocks][16][D]
