@@ -12,7 +12,9 @@ reported under "workloads".
 
 Consecutive steps cycle through --copies independent copies of every input
 (cache, block table, queries, weights), so the 256 MB Infinity Cache cannot
-serve a step from the previous one.  The timed region replays one HIP graph
+serve a step from the previous one.  After the --warmup steps, untimed steps
+run for --settle-ms of wall time (the first tens of milliseconds of sustained
+load run slower than the steady state).  The timed region replays one HIP graph
 per input copy holding the step's kernels (--eager launches them from the
 host instead); the decode call's own duration for the roofline comes from
 HIP events on its stream around each call.  The CPU baseline runs the oracle
@@ -426,7 +428,24 @@ def decode_figures_only(figs):
     return {k: figs[k] for k in ("decode_bytes", "decode_flops", "kv_bytes", "tokens_heads")}
 
 
-def measure(name: str, steps: int, warmup: int, n_copies: int, num_splits: int, eager: bool, with_ev: bool = True):
+def settle(run_one, settle_ms: float) -> int:
+    """Untimed steps until `settle_ms` of wall time has passed.  The first tens
+    of milliseconds of sustained load after a pause run 15-25 % slower than the
+    steady state on this part (the same kernels, graph-replayed or launched from
+    the host), so the timed region starts after them.  Returns the step count."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            run_one(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def measure(name: str, steps: int, warmup: int, n_copies: int, num_splits: int, eager: bool, with_ev: bool = True,
+            settle_ms: float = 0.0):
     """Time one workload: the whole step (absorb -> decode -> decompress, or
     the decode call alone when the absorbed queries are given) replayed from
     HIP graphs over `n_copies` input copies, and the decode call alone with
@@ -505,6 +524,10 @@ def measure(name: str, steps: int, warmup: int, n_copies: int, num_splits: int, 
         for k in range(max(1, warmup)):
             graphs[k % len(graphs)].replay()
         torch.cuda.synchronize()
+    if settle_ms > 0:
+        n_settle = settle(lambda k: graphs[k % len(graphs)].replay() if graphs else step(copies[k % len(copies)]),
+                          settle_ms)
+        log(f"{spec.name}: {n_settle} untimed steps over {settle_ms:.0f} ms before the timed region")
 
     # Timed region: the whole step, K times.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -560,6 +583,7 @@ def measure(name: str, steps: int, warmup: int, n_copies: int, num_splits: int, 
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "decode_us": round(dec_avg * 1e3, 2), "decode_min_us": round(dec_ms[0] * 1e3, 2),
         "decode_bytes": figs["decode_bytes"], "decode_flops": figs["decode_flops"],
+        "decode_traffic": measured_traffic(spec.name),
         "decode_gbs": round(dec_gbs, 2), "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_tflops": round(dec_tflops, 2), "decode_mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
         "bound": "mfma" if figs["decode_flops"] / figs["decode_bytes"] > BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3
@@ -598,6 +622,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="after the warmup steps, untimed steps for this much wall time before each timed region "
+                         "(sustained load runs slower for its first tens of milliseconds)")
     ap.add_argument("--workload", default="dsv3_ragged")
     ap.add_argument("--extra-workloads", default="glm52_decode,glm52_causal_tq4,nope_long,nope_wide",
                     help="comma-separated workloads also timed and reported under 'workloads' ('' for none)")
@@ -632,7 +659,7 @@ def main() -> int:
     torch.cuda.set_device(0)
 
     main_rec, figs, case, copies, stream = measure(args.workload, args.steps, args.warmup, args.copies,
-                                                   args.num_splits, args.eager)
+                                                   args.num_splits, args.eager, settle_ms=args.settle_ms)
     spec = mi.SPECS[args.workload]
     dims = (spec.n_head, spec.d_nope, spec.d_rope, spec.d_v, spec.kv_rank)
 
@@ -641,7 +668,8 @@ def main() -> int:
     extra_names = [w for w in args.extra_workloads.split(",") if w and w != args.workload]
     sub = {}
     for w in extra_names:
-        rec, f2, c2, cp2, _ = measure(w, args.steps, args.warmup, min(args.copies, 2), args.num_splits, args.eager)
+        rec, f2, c2, cp2, _ = measure(w, args.steps, args.warmup, min(args.copies, 2), args.num_splits, args.eager,
+                                  settle_ms=args.settle_ms)
         extras[w] = rec
         s2 = mi.SPECS[w]
         if w == "glm52_decode":
@@ -674,6 +702,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
