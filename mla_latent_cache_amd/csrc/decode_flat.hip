@@ -646,7 +646,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
       // Every wave votes; a second pass if any query row of the workgroup
       // needs one (the tile loads are shared, so all waves go again).
       if (pass > 0) break;
-      if (lane == 0) vote[w] = __ballot(over) != 0 ? 1 : 0;
+      {
+        // The ballot with every lane active (inside the lane-0 branch it
+        // would see lane 0 alone).
+        const int any_over = __ballot(over) != 0 ? 1 : 0;
+        if (lane == 0) vote[w] = any_over;
+      }
       barrier_keep_loads();
       int redo = 0;
 #pragma unroll
@@ -822,9 +827,9 @@ FlatPlan flat_plan(int n_head, int d_rope, int batch, int t_q, int max_blocks, i
   (void)d_rope;
   FlatPlan p = {};
   const int64_t n_q = (int64_t)t_q * n_head;
-  // 128 query rows per workgroup (eight waves) from 128 query rows per
-  // request on, else 64 (four waves); the query tiles of one range share an
-  // XCD, so a cache tile is fetched from HBM once and from L2 by the rest.
+  // 128 query rows per workgroup (four waves of 32); the query tiles of one
+  // range share an XCD, so a cache tile is fetched from HBM once and from L2
+  // by the rest.
   p.qb = kWaves;  // waves per workgroup
   p.qt = 32 * kWaves;
   p.m_tiles = (int)((n_q + p.qt - 1) / p.qt);

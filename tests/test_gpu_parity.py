@@ -291,16 +291,32 @@ def test_flat_schedule_split_invariance_and_determinism():
     full_compare(case, run(dc, num_splits=64))
 
 
-def test_score_growth_far_past_the_first_tile_every_element():
-    # The rope columns of late rows of two requests are scaled by 200, so
-    # their scores exceed those of the request's first tile by far more than
-    # the 128-row kernel's fixed softmax reference allows (64 in log2 units):
+@pytest.mark.parametrize("heads,t_q", [(32, 1), (16, 2), (8, 4)])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_split_kernel_below_64_query_rows_every_element(heads, t_q, num_splits):
+    # Fewer than 64 query rows per request (heads x queries) take the
+    # per-request split kernel instead of the length-balanced one; GLM-5.2
+    # head dimensions, causal multi-token queries, every element compared.
+    lens = (700, 0, 1000, 33, 257)
+    spec = spec_small(f"glm52_h{heads}_t{t_q}", "glm52_decode", n_head=heads, t_q=t_q, batch=len(lens),
+                      fixed_lens=lens, max_blocks=64)
+    case = mi.make_case(spec)
+    res = run(DeviceCase(case), num_splits=num_splits)
+    assert res["status"] == 0
+    full_compare(case, res)
+
+
+@pytest.mark.parametrize("base", ["dsv3_ragged", "glm52_decode"])
+def test_score_growth_far_past_the_first_tile_every_element(base):
+    # 128 (DeepSeek-shaped) or 64 (GLM-5.2) query rows per request.  The rope
+    # columns of late rows of two requests are scaled by 200, so their scores exceed those of the request's first tile by far more than
+    # the length-balanced kernel's fixed softmax reference allows (64 in log2 units):
     # the pieces holding the jump are streamed a second time with their true
     # maximum.  A third request grows by 18-41 (no second pass; probabilities
     # up to 2^41 before normalisation).  The value columns are untouched.
     # Every element is compared, for range counts that cut the requests at
     # different places.
-    spec = spec_small("dsv3_growth", "dsv3_ragged", batch=4, fixed_lens=(700, 1000, 33, 257), max_blocks=64,
+    spec = spec_small(f"{base}_growth", base, batch=4, fixed_lens=(700, 1000, 33, 257), max_blocks=64,
                       lengths="fixed", zero_requests=())
     case = mi.make_case(spec)
     kv = mi.bf16_bits_to_f32(case.kv)
@@ -309,6 +325,31 @@ def test_score_growth_far_past_the_first_tile_every_element():
             kv[case.block_table[b, j // 16], j % 16, spec.kv_rank:] *= f
     case.kv[...] = mi.to_bf16_bits(kv)
     for k in (1, 3, 0):
+        res = run(DeviceCase(case), num_splits=k)
+        assert res["status"] == 0
+        full_compare(case, res)
+
+
+@pytest.mark.parametrize("base", ["dsv3_ragged", "glm52_decode"])
+def test_second_pass_covers_rows_other_than_the_first_every_element(base):
+    # Only some query rows see a jump: the rope columns of late rows of request
+    # 1 are scaled by 200, and the rope part of the queries of heads 0, 32, 64
+    # and 96 (the first row of each 32-row wave) is zero, so those rows' scores
+    # do not grow while every other row's do.  Any row past the softmax
+    # reference's limit must send the workgroup round a second time.
+    spec = spec_small(f"{base}_quiet", base, batch=3, fixed_lens=(700, 1000, 257), max_blocks=64,
+                      lengths="fixed", zero_requests=())
+    case = mi.make_case(spec)
+    kv = mi.bf16_bits_to_f32(case.kv)
+    for j in range(300, int(case.seq_lens[1])):
+        kv[case.block_table[1, j // 16], j % 16, spec.kv_rank:] *= 200.0
+    case.kv[...] = mi.to_bf16_bits(kv)
+    quiet = list(range(0, spec.n_head, 32))
+    if spec.q_given:
+        case.q_abs[:, :, quiet, spec.kv_rank:] = 0
+    else:
+        case.q_pe[:, quiet, :] = 0
+    for k in (1, 3, 5, 0):
         res = run(DeviceCase(case), num_splits=k)
         assert res["status"] == 0
         full_compare(case, res)
