@@ -93,6 +93,25 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 products whose accumulator lives in vector registers (the output
+// accumulators fill the matrix-core registers, and the softmax reads the scores
+// with vector instructions).  Written as assembly, so the compiler does not
+// move the accumulator into matrix-core registers; it also does not know the
+// products' latency, so a chain ends with mfma_vacc_drain() before anything
+// else reads the accumulator.  Each product of a chain accumulates into the
+// registers the previous one wrote, which the hardware forwards back to back.
+__device__ __forceinline__ void mfma_vacc_first(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vacc(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// 20 wait states: more than any matrix product needs before a vector
+// instruction may read its result.
+__device__ __forceinline__ void mfma_vacc_drain(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(c));
+}
+
 // Position within the tile (block * 16 + row) of the tile row that output row
 // i of S^T = K Q^T stands for.  The products see the 32 rows in this order;
 // it makes every group of 4 rows that one transposing V^T read covers
@@ -336,7 +355,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
     }
     const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
     slot_bad = (slot_bad & ~(1u << slot)) | (badbit << slot);
-    lbase = ring_base + slot * (uint32_t)T::IMG_BYTES;
+    lbase = __builtin_amdgcn_readfirstlane(ring_base + slot * (uint32_t)T::IMG_BYTES);  // scalar: M0 of the loads
   };
   // The first kRing - 1 tiles in flight, and the block ids of the next.
   int k_next = t0;
@@ -528,7 +547,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
         // products (launch of tile k + 3 in step 0, the block ids of the tile
         // after it in step 2), and this wave's loads of tile k + 3 go out one
         // per odd step.
-        f32x16 sacc = {};
+        f32x16 sacc;
         {
           constexpr int kAhead = kKAhead;
           constexpr int DSTEP = KS / 2 / LJ;  // two-read steps between two tile loads
@@ -544,8 +563,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
                constexpr int I = 2 * J;
                constexpr int issued = I + kAhead < KS ? I + kAhead : KS;
                lgkm_wait<issued - 2 - I>(kr[I], kr[I + 1]);
-               sacc = mfma32x32x16(as_bf16x8(kr[I]), qf[I], sacc);
-               sacc = mfma32x32x16(as_bf16x8(kr[I + 1]), qf[I + 1], sacc);
+               if constexpr (I == 0)
+                 mfma_vacc_first(sacc, as_bf16x8(kr[I]), qf[I]);
+               else
+                 mfma_vacc(sacc, as_bf16x8(kr[I]), qf[I]);
+               mfma_vacc(sacc, as_bf16x8(kr[I + 1]), qf[I + 1]);
                if constexpr (I + kAhead < KS) {
                  constexpr int P = I + kAhead;
                  lds_b128<128 * (P / 4)>(kaddr[P % 4], kr[P]);
@@ -565,6 +587,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
              ...);
           }(std::make_integer_sequence<int, KS / 2>{});
         }
+
+        mfma_vacc_drain(sacc);
 
         // Softmax of the lane's query over its 16 tile rows (element v is tile
         // position 8 (v / 4) + 2 h + {0, 1, 4, 5}[v % 4]; the other 16 rows sit
