@@ -225,17 +225,21 @@ __device__ FlatRange flat_range(const FlatArgs& a, int g) {
 __device__ __forceinline__ int range_of(int64_t t, int64_t T, int G) { return (int)(((t + 1) * G - 1) / T); }
 
 // A request cursor: request b starts at tile p of the sequence and has n tiles
-// and L rows here.
+// and L rows here (L <= Lg, a 32-bit length); row is its block-table row.
 struct Cursor {
   int b, n, p;
-  int64_t L, Lg;
+  int L, Lg;
   uint32_t f;
+  const const_i32* row;
 };
 
 __device__ __forceinline__ void cursor_load(const FlatArgs& a, Cursor& c) {
   const const_i32* sl = (const const_i32*)a.seq_lens;
   c.Lg = sl[c.b];
-  c.n = req_tiles(a, c.Lg, c.L, c.f);
+  int64_t L;
+  c.n = req_tiles(a, c.Lg, L, c.f);
+  c.L = (int)L;
+  c.row = (const const_i32*)a.bt + (int64_t)c.b * a.max_blocks;
 }
 
 // Four waves (one per SIMD), 128 query rows per workgroup: wave w owns query
@@ -287,36 +291,38 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
   }
 
   const uint16_t* kv = static_cast<const uint16_t*>(a.kv);
-  const const_i32* bt_s = (const const_i32*)a.bt;
   const uint32_t nb32 = a.num_blocks < (int64_t)INT32_MAX ? (uint32_t)a.num_blocks : (uint32_t)INT32_MAX;
 
-  // Tile loads: wave w issues the 1 KB wave-loads u = w + kWaves j of a tile
-  // image; load u covers chunk slots [64 u', 64 u' + 64) of block u / BLK_LOADS
-  // (u' = u % BLK_LOADS).  vo[j]: global byte offset (within its block) of this
-  // lane's 16 bytes of load j; padding slots get an offset past any block
-  // (they read zeros).
-  constexpr int LJ = T::TILE_LOADS / kWaves;  // loads per wave per tile
-  static_assert(T::TILE_LOADS % kWaves == 0, "whole loads per wave");
+  // Tile loads: wave w loads half w % 2 of block my_hb = w / 2 of a tile
+  // image, the 1 KB wave-loads u = LJ (w % 2) + j of that block, load u
+  // covering chunk slots [64 u, 64 u + 64) of the block image.  vo[j]: global
+  // byte offset (within the block) of this lane's 16 bytes of load j; padding
+  // slots get an offset past any block (they read zeros).
+  constexpr int LJ = T::BLK_LOADS / 2;  // loads per wave per tile
+  static_assert(kWaves == 4 && T::BLK_LOADS % 2 == 0 && 2 * LJ * 2 == T::TILE_LOADS, "two waves per block");
+  const int my_hb = w >> 1;
   uint32_t vo[LJ];
 #pragma unroll
   for (int j = 0; j < LJ; ++j) {
-    const int u = w + kWaves * j;
-    const int hb = u / T::BLK_LOADS;
-    const int pos = (u - hb * T::BLK_LOADS) * 64 + lane;
+    const int pos = (LJ * (w & 1) + j) * 64 + lane;
     const int rl = pos / STRIDE;
     const int c = (pos - rl * STRIDE) ^ (rl & 7);
     vo[j] = c < CH ? (uint32_t)(rl * D + c * 8) * 2u : 0x7ffffff0u;
   }
   const uint32_t ring_base = lds_addr(ring);
+  // This wave's part of a tile image: its block's image, then its half.
+  const uint32_t wave_img = (my_hb ? (uint32_t)T::BLK1 : 0u) + (uint32_t)(LJ * (w & 1)) * 1024u;
 
   // Producer: fetch(k) finds the request holding tile k, issues the scalar
   // loads of its two block ids and notes how many rows of each block are
-  // valid; it runs one tile step ahead of launch(k), which forms one buffer
-  // resource per block (sized to its valid rows), picks the tile's ring slot
-  // and records in slot_bad whether a block id of the tile was outside the
-  // cache.  The S step then issues this wave's 1 KB loads one at a time
-  // (dma_part), so that the memory pipeline takes them while the matrix
-  // cores work.
+  // valid; it runs one tile step ahead of launch(k), which forms the buffer
+  // resource of this wave's block (sized to its valid rows), picks the
+  // tile's ring slot and records in slot_bad whether a block id of the tile
+  // was outside the cache.  The S step then issues this wave's 1 KB loads one
+  // at a time (dma_part), so that the memory pipeline takes them while the
+  // matrix cores work.  Every tile step launches one tile: past the range's
+  // last tile the resource is empty, so the loads deliver zeros into the free
+  // image, and every wait counts the same loads.
   Cursor prod;
   prod.b = R.b_first;
   prod.p = R.p_first;
@@ -331,37 +337,34 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
       cursor_load(a, prod);
     }
     const int pkl = k - prod.p;
-    const int64_t left = prod.L - 32 * (int64_t)pkl;  // rows of the request from this tile on (> 0)
-    const const_i32* row = bt_s + (int64_t)prod.b * a.max_blocks + 2 * pkl;
+    const int left = prod.L - 32 * pkl;  // rows of the request from this tile on (> 0)
+    const const_i32* row = prod.row + 2 * pkl;
     pid[0] = row[0];
-    pnv[0] = left >= 16 ? 16 : (int)left;
-    pnv[1] = left >= 32 ? 16 : (left > 16 ? (int)left - 16 : 0);
+    pnv[0] = left >= 16 ? 16 : left;
+    pnv[1] = left >= 32 ? 16 : (left > 16 ? left - 16 : 0);
     pid[1] = pnv[1] > 0 ? row[1] : -1;
   };
-  i32x4 lrs[2];
+  i32x4 lrs;
   uint32_t lbase = 0;
-  auto dma_part = [&](int j) {
-    const int u = w + kWaves * j;
-    const bool blk0 = kWaves * j + kWaves - 1 < T::BLK_LOADS || (kWaves * j < T::BLK_LOADS && u < T::BLK_LOADS);
-    dma16(blk0 ? lrs[0] : lrs[1], lbase + (uint32_t)u * 1024u + (blk0 ? 0u : 128u), vo[j]);
-  };
+  auto dma_part = [&](int j) { dma16(lrs, lbase + (uint32_t)j * 1024u, vo[j]); };
   auto launch = [&](int k) {
-    uint32_t badbit = 0;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const bool ok = (uint32_t)pid[hb] < nb32;
-      if (pnv[hb] > 0 && !ok) badbit = 1u;
-      lrs[hb] = raw_rsrc(kv + (int64_t)(ok ? pid[hb] : 0) * (16 * D), ok ? (uint32_t)(pnv[hb] * D * 2) : 0u);
-    }
+    const bool real = k < t1;
+    const bool bad0 = pnv[0] > 0 && (uint32_t)pid[0] >= nb32, bad1 = pnv[1] > 0 && (uint32_t)pid[1] >= nb32;
+    const uint32_t badbit = real && (bad0 || bad1) ? 1u : 0u;
+    const int32_t id = my_hb ? pid[1] : pid[0];
+    const int nv = my_hb ? pnv[1] : pnv[0];
+    const bool ok = real && (uint32_t)id < nb32;
+    lrs = raw_rsrc(kv + (ok ? (int64_t)(uint32_t)id * (16 * D) : 0), ok ? (uint32_t)(nv * D * 2) : 0u);
     const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
     slot_bad = (slot_bad & ~(1u << slot)) | (badbit << slot);
-    lbase = __builtin_amdgcn_readfirstlane(ring_base + slot * (uint32_t)T::IMG_BYTES);  // scalar: M0 of the loads
+    // Scalar: the M0 base of this wave's loads.
+    lbase = __builtin_amdgcn_readfirstlane(ring_base + slot * (uint32_t)T::IMG_BYTES + wave_img);
   };
   // The first kRing - 1 tiles in flight, and the block ids of the next.
   int k_next = t0;
   auto prologue = [&]() {
-    for (int s = 0; s < kRing - 1 && k_next < t1; ++s) {
-      fetch(k_next);
+    for (int s = 0; s < kRing - 1; ++s) {
+      if (k_next < t1) fetch(k_next);
       launch(k_next++);
 #pragma unroll
       for (int j = 0; j < LJ; ++j) dma_part(j);
@@ -524,18 +527,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
 
       for (int k = ka; k < ke; ++k) {
         // Tile k resident: this wave's loads of it are done once at most the
-        // loads of the tiles issued after it (k + 1, k + 2) are outstanding
-        // (the first tile of a pass was waited for before the loop).
-        if (k != ka) {
-          if (k + 2 < t1)
-            wait_vmcnt<2 * LJ>();
-          else if (k + 1 < t1)
-            wait_vmcnt<LJ>();
-          else
-            wait_vmcnt<0>();
-        }
+        // loads of the two tiles issued after it are outstanding (the first
+        // tile of a pass was waited for before the loop).
+        if (k != ka) wait_vmcnt<2 * LJ>();
         barrier_keep_loads();  // tile k visible to all waves; tile k - 1 no longer read
-        const bool loading = k_next < t1;
         const int kl = k - cons.p;
         const uint32_t slot = (uint32_t)(k - t0) & (kRing - 1);
         if ((slot_bad >> slot) & 1u) bad = true;
@@ -546,7 +541,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
         // time.  The scalar work of the producer runs among the first
         // products (launch of tile k + 3 in step 0, the block ids of the tile
         // after it in step 2), and this wave's loads of tile k + 3 go out one
-        // per odd step.
+        // per odd step (zero-size past the range's last tile).
         f32x16 sacc;
         {
           constexpr int kAhead = kKAhead;
@@ -573,15 +568,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
                  lds_b128<128 * (P / 4)>(kaddr[P % 4], kr[P]);
                  lds_b128<128 * ((P + 1) / 4)>(kaddr[(P + 1) % 4], kr[P + 1]);
                }
-               if constexpr (J == 0) {
-                 if (loading) launch(k_next++);
-               }
+               if constexpr (J == 0) launch(k_next++);
                if constexpr (J == 2) {
                  if (k_next < t1) fetch(k_next);  // block ids of the tile the next step issues
                }
-               if constexpr (J % DSTEP == DSTEP / 2 && J / DSTEP < LJ) {
-                 if (loading) dma_part(J / DSTEP);
-               }
+               if constexpr (J % DSTEP == DSTEP / 2 && J / DSTEP < LJ) dma_part(J / DSTEP);
                __builtin_amdgcn_sched_barrier(0);
              }()),
              ...);
@@ -691,12 +682,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_flat_mfma(const FlatArg
       cursor_load(a, prod);
       k_next = ka;
       prologue();
-      if (ka + 2 < t1)
-        wait_vmcnt<2 * LJ>();
-      else if (ka + 1 < t1)
-        wait_vmcnt<LJ>();
-      else
-        wait_vmcnt<0>();
+      wait_vmcnt<2 * LJ>();
       m_ref = m_hi;
     }
 
