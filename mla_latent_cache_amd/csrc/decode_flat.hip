@@ -744,6 +744,55 @@ __global__ __launch_bounds__(64 * (W > 1 ? W : kMergeRows)) void decode_flat_mer
   auto pidx = [&](int k) { return ((int64_t)(g0 + k) * a.m_tiles + mt) * 2 + (k == 0 ? s0 : 0); };
   auto lse_of = [&](int k) { return a.lse_part[pidx(k) * a.qt + ql]; };
 
+  if (W == 1 && P <= 8) {
+    // Up to eight pieces: every load (the pieces' LSEs, one per lane, and
+    // their outputs, lane l owning columns 8 l .. 8 l + 7) goes out at once,
+    // then the weights.  Pieces are added in index order.
+    const float ls = lane < P ? lse_of(lane) : -INFINITY;
+    f32x4 xa[8], xb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      xa[u] = xb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (u < P) {
+        const int64_t base = (pidx(u) * a.qt + ql) * 512 + 8 * lane;
+        if (a.out_bf16) {
+          const uint4 r = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.o_part) + base);
+          xa[u] = bf16x4_to_f32(uint2{r.x, r.y});
+          xb[u] = bf16x4_to_f32(uint2{r.z, r.w});
+        } else {
+          xa[u] = *reinterpret_cast<const f32x4*>(a.o_part + base);
+          xb[u] = *reinterpret_cast<const f32x4*>(a.o_part + base + 4);
+        }
+      }
+    }
+    const float M = wmax(ls);
+    const bool any_nan = __ballot(isnan(ls)) != 0;
+    float wtot = 0.f;
+    f32x4 oa = {0.f, 0.f, 0.f, 0.f}, ob = oa;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float lu = __shfl(ls, u, 64);
+      const bool live = u < P && lu != -INFINITY && M != -INFINITY;  // an empty piece may hold anything
+      const float wgt = live ? __expf(lu - M) : 0.f;
+      wtot += wgt;
+      oa += wgt * (live ? xa[u] : f32x4{0.f, 0.f, 0.f, 0.f});
+      ob += wgt * (live ? xb[u] : f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
+    const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+    const f32x4 ra = any_nan ? nan4 : oa * inv, rb = any_nan ? nan4 : ob * inv;
+    if (a.out_bf16) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + qrow * 512 + 8 * lane) =
+          uint4{pack_bf16x2(ra[0], ra[1]), pack_bf16x2(ra[2], ra[3]), pack_bf16x2(rb[0], rb[1]), pack_bf16x2(rb[2], rb[3])};
+    } else {
+      float* o = static_cast<float*>(a.out) + qrow * 512 + 8 * lane;
+      *reinterpret_cast<f32x4*>(o) = ra;
+      *reinterpret_cast<f32x4*>(o + 4) = rb;
+    }
+    if (lane == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wtot));
+    return;
+  }
+
   const int wv = W > 1 ? v : 0;
   const int k0 = (int)((int64_t)P * wv / W), k1 = (int)((int64_t)P * (wv + 1) / W);
   // Maximum LSE and NaN over all pieces (every wave scans all of them).
