@@ -906,6 +906,110 @@ __global__ __launch_bounds__(64 * kWideWaves) void decode_merge_wide(const Decod
   if (tid == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
 }
 
+// The same merge for kv_rank 512, with each row's columns split over
+// kWideCols workgroups (128 columns each), so that a few long rows still
+// spread their partials over every compute unit.  Wave v sums the splits
+// [v S / W, (v + 1) S / W): lanes 0-31 take the even splits of that run and
+// lanes 32-63 the odd ones, four columns per lane, and the two halves are
+// added before the per-wave sums are added in wave order through LDS.
+// Workgroup i handles column chunk i / rows of row i % rows (rows = batch x
+// query rows), so with a row count that is a multiple of 8 a row's chunks run
+// on the XCD the row's other workgroups use.
+constexpr int kWideCols = 4;
+
+__global__ __launch_bounds__(64 * kWideWaves) void decode_merge_wide512(const DecodeArgs a) {
+  constexpr int R = 512, CW = R / kWideCols;
+  static_assert(CW == 128, "32 lanes x 4 columns per chunk");
+  __shared__ __attribute__((aligned(16))) f32x4 wsum_lds[kWideWaves][CW / 4];
+  __shared__ float red[kWideWaves];
+  const int tid = threadIdx.x, lane = tid & 63, v = tid >> 6;
+  const int64_t rows = (int64_t)a.batch * a.n_q;
+  const int chunk = (int)(blockIdx.x / rows);
+  const int64_t rid = blockIdx.x - (int64_t)chunk * rows;
+  int64_t qrow;
+  if (a.batch % 8 == 0) {  // request b on XCD b % 8, as in decode_merge
+    const int64_t rest = rid >> 3;
+    const int64_t bg = rest / a.n_q;
+    qrow = (bg * 8 + (rid & 7)) * a.n_q + (rest - bg * a.n_q);
+  } else {
+    qrow = rid;
+  }
+  const int b = (int)(qrow / a.n_q);
+  const int q = (int)(qrow - (int64_t)b * a.n_q);
+  const int S = a.splits;
+  const float* lp = a.lse_part + (int64_t)b * S * a.n_q + q;
+
+  float mx = -INFINITY;
+  bool nan_seen = false;
+  for (int k = tid; k < S; k += 64 * kWideWaves) {
+    const float x = lp[(int64_t)k * a.n_q];
+    nan_seen |= isnan(x);
+    mx = fmaxf(mx, x);
+  }
+  mx = wave_max(mx);
+  const int any_nan = __syncthreads_or(nan_seen ? 1 : 0);
+  if (lane == 0) red[v] = mx;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int i = 0; i < kWideWaves; ++i) M = fmaxf(M, red[i]);
+  __syncthreads();
+  float wpart = 0.f;
+  if (M != -INFINITY)
+    for (int k = tid; k < S; k += 64 * kWideWaves) wpart += __expf(lp[(int64_t)k * a.n_q] - M);
+  wpart = wave_sum(wpart);
+  if (lane == 0) red[v] = wpart;
+  __syncthreads();
+  float wsum = 0.f;
+  for (int i = 0; i < kWideWaves; ++i) wsum += red[i];
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+
+  const int k0 = (int)((int64_t)S * v / kWideWaves), k1 = (int)((int64_t)S * (v + 1) / kWideWaves);
+  const int hl = lane >> 5;                              // split parity of this lane half
+  const int c0 = chunk * CW + 4 * (lane & 31);           // this lane's four columns
+  const float* op = a.o_part + ((int64_t)b * S * a.n_q + q) * R + c0;
+  const int64_t sstride = (int64_t)a.n_q * R;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    // Splits k0 + hl, k0 + hl + 2, ...: four at a time per lane half.
+    int k = k0 + hl;
+    for (; k + 6 < k1; k += 8) {
+      f32x4 x[4];
+      float wk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wk[u] = lp[(int64_t)(k + 2 * u) * a.n_q];
+        x[u] = *reinterpret_cast<const f32x4*>(op + (k + 2 * u) * sstride);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool live = wk[u] != -INFINITY;  // an empty split may be unwritten
+        o += (live ? __expf(wk[u] - M) : 0.f) * (live ? x[u] : f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+    }
+    for (; k < k1; k += 2) {
+      const float wk = lp[(int64_t)k * a.n_q];
+      if (wk != -INFINITY) o += __expf(wk - M) * *reinterpret_cast<const f32x4*>(op + k * sstride);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], 32, 64);
+  if (hl == 0) wsum_lds[v][lane] = o;
+  __syncthreads();
+  if (v == 0 && hl == 0) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kWideWaves; ++i) acc += wsum_lds[i][lane];
+    const f32x4 nan4 = {NAN, NAN, NAN, NAN};
+    const f32x4 val = any_nan ? nan4 : acc * inv;
+    if (a.out_bf16) {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + qrow * R + c0) =
+          uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + qrow * R + c0) = val;
+    }
+  }
+  if (chunk == 0 && tid == 0 && a.lse) a.lse[qrow] = any_nan ? NAN : (M == -INFINITY ? -INFINITY : M + __logf(wsum));
+}
+
 // LSE combine of P partial results over disjoint row sets (the split merge,
 // here across context-parallel ranks): one wave per row.  With M the largest
 // part LSE and w_p = exp(lse_p - M), o = sum_p w_p o_p / sum_p w_p and
@@ -1043,6 +1147,11 @@ hipError_t launch_decode(const DecodeArgs& a, bool mfma, bool bf16, hipStream_t 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.direct || a.batch == 0) return e;
   const int64_t rows = (int64_t)a.batch * a.n_q;
+  if (a.splits >= kWideMinSplits && a.kv_rank == 512) {
+    if (rows * kWideCols > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(decode_merge_wide512, dim3((unsigned)(rows * kWideCols)), dim3(64 * kWideWaves), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.splits >= kWideMinSplits) {
     const size_t lds = ((size_t)kWideWaves * a.kv_rank + kWideWaves) * sizeof(float);
     hipLaunchKernelGGL(decode_merge_wide, dim3((unsigned)rows), dim3(64 * kWideWaves), lds, stream, a);
