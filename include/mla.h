@@ -258,8 +258,9 @@ mla_status mla_lse_combine(int32_t width, int64_t n_rows, int32_t n_parts, const
  * mla_attend_absorbed, decompress step):
  *   out[n][h][j] = sum_l w_uv[h][j][l] * o_lat[n][h][l]
  * o_lat [n_tok][n_head][kv_rank] type o_dt, w_uv [n_head][d_v][kv_rank] type
- * w_dt, out [n_tok][n_head][d_v] type out_dt.  Float32 accumulation.  Every
- * tensor pointer must be 16-byte aligned.
+ * w_dt, out [n_tok][n_head][d_v] type out_dt.  Float32 accumulation; with
+ * bf16 weights, float32 o_lat values are rounded to bf16 (nearest even) before
+ * the products.  Every tensor pointer must be 16-byte aligned.
  * Errors: MLA_ERR_NULL, MLA_ERR_DIMS (n_head, d_v, kv_rank < 1), MLA_ERR_SHAPE
  * (n_tok < 0), MLA_ERR_ARG (bad dtype code, misaligned pointer), MLA_ERR_HIP. */
 mla_status mla_decompress_v(const mla_dims* dims, int64_t n_tok, const void* o_lat,

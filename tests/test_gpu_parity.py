@@ -87,9 +87,9 @@ def test_small_bf16_every_element(name, num_splits):
 
 def test_absorb_and_decompress_over_several_token_chunks():
     # 150 query rows (75 requests x 2 queries): the absorb and decompression
-    # kernels stage tokens 64 at a time, so this runs two full chunks and a
-    # ragged third one (22 rows: one full 16-row tile and 6 more); every element
-    # of q_abs, o_lat and out is compared.
+    # kernels give each group of 64 tokens its own workgroups, so this runs two
+    # full groups and a ragged third one (22 rows: one full 16-row tile and 6
+    # more); every element of q_abs, o_lat and out is compared.
     lens = tuple(2 + (7 * i) % 40 for i in range(75))
     spec = spec_small("glm52_many_tokens", "glm52_decode", batch=75, t_q=2, fixed_lens=lens, max_blocks=3)
     case = mi.make_case(spec)
@@ -99,10 +99,9 @@ def test_absorb_and_decompress_over_several_token_chunks():
 
 
 def test_many_token_instances_give_the_same_bits():
-    # Above one 64-token chunk (absorb) or 32 tokens (decompression) the
-    # kernels run the chunk's token tiles as independent accumulator chains;
-    # every output is still the same sequence of products, so the leading
-    # tokens of a wider call must match the narrower call bit for bit.
+    # A token's outputs are the same sequence of products whatever else the
+    # call holds (the other tokens of its 64-token group, or other groups), so
+    # the leading tokens of a wider call must match the narrower call bit for bit.
     torch.manual_seed(11)
     H, DN, R, DV, KR = 64, 192, 64, 256, 512
     dims = (H, DN, R, DV, KR)
@@ -123,6 +122,54 @@ def test_many_token_instances_give_the_same_bits():
         torch.cuda.synchronize()
         assert torch.equal(qa_w[:narrow_a], qa_n)
         assert torch.equal(out_w[:narrow_d], out_n)
+
+
+# (n_head, d_nope, d_rope, d_v, kv_rank): contraction lengths of 1, 3, 4, 6, 8
+# and 16 k-steps of 32, rope widths copied 16 bytes (8, 64) or one element
+# (4, 12) at a time or absent, d_v not a multiple of the 64-row slice.
+GEMM_GEOMS = {
+    "glm52": (64, 192, 64, 256, 512),
+    "dsv3_heads16": (16, 128, 64, 128, 512),
+    "ks3": (8, 96, 8, 64, 256),
+    "ks16_nope": (4, 512, 0, 64, 512),
+    "rope4_dv40": (4, 64, 4, 40, 128),
+    "ks1_rope12": (3, 32, 12, 36, 64),
+}
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("n_tok", [1, 17, 64, 65, 150])
+@pytest.mark.parametrize("geom", sorted(GEMM_GEOMS))
+def test_absorb_and_decompress_every_element(geom, n_tok):
+    """Every element of q_abs and out against the oracle's absorb and
+    decompress, for bf16 and float32 outputs and float32 activations (which
+    the kernels round to bf16 before the products, as the header states)."""
+    H, DN, R, DV, KR = GEMM_GEOMS[geom]
+    dims = (H, DN, R, DV, KR)
+    d = oracle.Dims(H, DN, R, DV, KR)
+    g = torch.Generator().manual_seed(1000 * n_tok + DN + R)
+    qn = torch.randn(n_tok, H, DN, generator=g).bfloat16()
+    qp = torch.randn(n_tok, H, R, generator=g).bfloat16()
+    wuk = (torch.randn(H, DN, KR, generator=g) / DN ** 0.5).bfloat16()
+    wuv = (torch.randn(H, DV, KR, generator=g) / KR ** 0.5).bfloat16()
+    ol = torch.randn(n_tok, H, KR, generator=g)
+    qa_ref = oracle.absorb(d, _bits(qn), _bits(qp), _bits(wuk))
+    for odt, kind in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+        qa = torch.empty(n_tok, H, KR + R, dtype=odt, device=DEV)
+        mla.mla_absorb_q(dims, qn.to(DEV), qp.to(DEV) if R else None, wuk.to(DEV), qa)
+        torch.cuda.synchronize()
+        assert_close(to_host(qa), qa_ref, kind, f"q_abs ({odt})")
+    ol_b = ol.bfloat16()
+    out_ref = oracle.decompress(d, _bits(ol_b), _bits(wuv))
+    for src in (ol_b, ol):
+        for odt, kind in ((torch.bfloat16, "bf16"), (torch.float32, "f32")):
+            out = torch.empty(n_tok, H, DV, dtype=odt, device=DEV)
+            mla.mla_decompress_v(dims, src.to(DEV), wuv.to(DEV), out)
+            torch.cuda.synchronize()
+            assert_close(to_host(out), out_ref, kind, f"out ({src.dtype} in, {odt} out)")
 
 
 def test_boundary_lengths_and_empty_requests():
