@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void decompress_mfma(int H, int DV, int n_tok,
   const u32x4* arow = buf[1] + (16 * w + l16) * P + g;
 #pragma unroll
   for (int t = 0; t < KS; ++t) A[t] = as_bf16x8(arow[4 * t]);
-  barrier_keep_loads();  // every wave holds its weights: buffer 1 is free
+  if (gi + zs < ngroups) barrier_keep_loads();  // every wave holds its weights: buffer 1 is free
 
   for (int b = 0; gi < ngroups; gi += zs, b ^= 1) {
     const int m0 = gi * G, cnt = min(G, n_tok - m0);
