@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["decode.hip", "decode_flat.hip", "gemm.hip", "prolog.hip", "prefill.hip", "mlaprolog.hip", "mla_api.cpp"]
+SOURCES = ["decode.hip", "decode_flat.hip", "gemm.hip", "prolog.hip", "prefill.hip", "prefill_attend.hip", "mlaprolog.hip",
+           "mla_api.cpp"]
 LIB = os.path.join(PKG, "libmla_amd.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -30,10 +31,11 @@ FLAGS = [
 # Per-source additions.  The prefill attention kernel keeps 128 accumulator
 # registers across its tile loop and rescales them (vector work) on a rare
 # branch; with the matrix-register form of the MFMA the compiler copies all of
-# them to vector registers on every tile (about a quarter of the loop's
-# instructions).  The vector-register form keeps them where the vector unit
-# can reach them, with bitwise-identical results.
-EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# them to vector registers on every tile.  The vector-register form keeps them
+# where the vector unit can reach them, with bitwise-identical results (the
+# decompression GEMM beside it was tuned with the same form).
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "prefill_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
