@@ -19,7 +19,10 @@ BUILD = os.path.join(ROOT, "_build")
 OUT = os.path.join(BUILD, "sanitized")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANG = "/opt/rocm/llvm/bin/clang"
-OTHERS = ["decode.hip", "decode_flat.hip", "gemm.hip", "prolog.hip", "prefill.hip", "mlaprolog.hip"]
+sys.path.insert(0, ROOT)
+from mla_latent_cache_amd import build as _build  # noqa: E402  (the library's own source list)
+
+OTHERS = [s for s in _build.SOURCES if s != "mla_api.cpp"]
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
