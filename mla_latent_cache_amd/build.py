@@ -32,8 +32,7 @@ FLAGS = [
 # registers across its tile loop and rescales them (vector work) on a rare
 # branch; with the matrix-register form of the MFMA the compiler copies all of
 # them to vector registers on every tile.  The vector-register form keeps them
-# where the vector unit can reach them, with bitwise-identical results (the
-# decompression GEMM beside it was tuned with the same form).
+# where the vector unit can reach them, with bitwise-identical results.
 EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "prefill_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

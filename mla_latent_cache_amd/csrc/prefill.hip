@@ -49,8 +49,14 @@ template <int DR>
 __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a) {
   using G = PGeom<DR>;
   constexpr int KR = G::KR, D = G::D;
-  __shared__ __attribute__((aligned(16))) u32x4 sw[2][kGN * kGChunks];  // weight rows [128][64]
-  __shared__ __attribute__((aligned(16))) u32x4 sc[2][kGM * kGChunks];  // cache rows [128][64]
+  // Chunk buffers (weight rows [2][128][64], cache rows [2][128][64]), reused
+  // after the k loop as the output stage [128 cache rows][128 + 8 values].
+  constexpr int kStagePitch = kGN + 8;  // bf16 values per staged output row (16 bytes of padding)
+  constexpr int kLdsChunks = (kGM * kStagePitch * 2 / 16) > 4 * kGN * kGChunks ? kGM * kStagePitch * 2 / 16
+                                                                              : 4 * kGN * kGChunks;
+  __shared__ __attribute__((aligned(16))) u32x4 lds[kLdsChunks];
+  u32x4(*sw)[kGN * kGChunks] = reinterpret_cast<u32x4(*)[kGN * kGChunks]>(lds);
+  u32x4(*sc)[kGM * kGChunks] = reinterpret_cast<u32x4(*)[kGM * kGChunks]>(lds + 2 * kGN * kGChunks);
 
   // Workgroup i runs on XCD i % 8.  Each XCD takes whole groups of
   // a.wgroup weight tiles (group g on XCD g % 8) and, per group, walks every
@@ -149,21 +155,29 @@ __global__ __launch_bounds__(256, 2) void prefill_decompress(const PrefillArgs a
   }
 
   // out[n][m]: lane (l16, g) holds cache row m = 64 wm + 16 j + l16 and weight
-  // rows n = 64 wn + 16 i + 4 g .. + 3, four consecutive columns of one head.
+  // rows n = 64 wn + 16 i + 4 g .. + 3 in acc[i][j].  They go through LDS as
+  // rows m of 128 values n (the padding spreads the rows of one write over the
+  // banks), and leave as 16-byte pieces of eight consecutive columns of one
+  // head, whole lines of each (head, row) segment.
+  uint16_t* st = reinterpret_cast<uint16_t*>(lds);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 64 * wm + 16 * j + l16, n = 64 * wn + 16 * i + 4 * g;
+      *reinterpret_cast<uint2*>(st + m * kStagePitch + n) =
+          uint2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+    }
+  barrier_keep_loads();
   const int DW = is_k ? G::DN : G::DV;
   uint16_t* dst_base = is_k ? a.kw : a.vw;
   const int nb = is_k ? n0 : n0 - NK;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = 64 * wm + 16 * j + l16;
-    if (m >= rows) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = nb + 64 * wn + 16 * i + 4 * g;
-      const int h = n / DW, col = n - h * DW;
-      uint16_t* dst = dst_base + (((int64_t)b * a.n_head + h) * a.max_rows + m0 + m) * DW + col;
-      *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
-    }
+  for (int idx = tid; idx < rows * (kGN / 8); idx += 256) {
+    const int m = idx / (kGN / 8), c = idx - m * (kGN / 8);
+    const int n = nb + 8 * c;
+    const int h = n / DW, col = n - h * DW;
+    uint16_t* dst = dst_base + (((int64_t)b * a.n_head + h) * a.max_rows + m0 + m) * DW + col;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(st + m * kStagePitch + 8 * c);
   }
   if (flags && tid == 0) atomicOr(&a.status[b], flags);
 }
