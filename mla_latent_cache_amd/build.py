@@ -32,7 +32,9 @@ FLAGS = [
 # registers across its tile loop and rescales them (vector work) on a rare
 # branch; with the matrix-register form of the MFMA the compiler copies all of
 # them to vector registers on every tile.  The vector-register form keeps them
-# where the vector unit can reach them, with bitwise-identical results.
+# where the vector unit can reach them, with bitwise-identical results.  The
+# prefill decompression GEMM (64 accumulator registers per lane) was tuned with
+# the same form.
 EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "prefill_attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
