@@ -8,20 +8,23 @@
 //   out[n][h][j] = sum_l W_UV[h][j][l] * o_lat[n][h][l]
 //
 // Both are weight-read bound at decode batch sizes (a few to a few hundred
-// tokens against 12-17 MB of weights), so each weight element is read from
-// HBM once per 64-token group: one workgroup owns one head, a 64-column slice
-// of the weight and up to 64 tokens, issues every load it needs at once (one
-// memory round trip: at decode sizes the kernel is latency-bound, so the
-// workgroup never waits twice), and runs its 16x16x32 bf16 MFMA tiles from
-// registers and LDS.  The token groups of one (head, slice) sit on one XCD
-// (grid z is the slowest index and H x slices is a multiple of 8 at the usual
-// sizes), so their weight reads after the first come from that XCD's L2.
-// W_UV rows are contiguous along the contraction index, so its A operand is
-// loaded straight into VGPRs; W_UK is contiguous along the output index, so
-// its slice is copied into LDS by the buffer unit and read back with the
-// transposing ds_read_b64_tr_b16.  Token operands are copied into LDS in the
-// MFMA operand order (one 1 KB block per 16-token tile and k-step), so each
-// is one conflict-free 16-byte read per lane, shared by the four waves.
+// tokens against 12-17 MB of weights), and at the smallest of them bound by
+// latency: a workgroup issues every load it needs at once (one memory round
+// trip; it never waits twice) and runs 16x16x32 bf16 MFMA tiles from
+// registers and LDS.  Operands reach LDS through the buffer unit as whole
+// rows (whole cache lines), at a pitch of one 16-byte chunk more than the row
+// so that 16 rows' same chunk falls on 16 distinct bank groups; results leave
+// through an LDS stage as whole rows.
+//   * Absorb: one workgroup per head, 64-column slice of W_UK and 64-token
+//     group.  W_UK is contiguous along the output index, so its slice is read
+//     back from LDS with the transposing ds_read_b64_tr_b16.  The token groups
+//     of one (head, slice) sit on one XCD (grid z is the slowest index and
+//     H x slices is a multiple of 8 at the usual sizes), so their weight reads
+//     after the first come from that XCD's L2.
+//   * Decompress: one workgroup per head and 64-row slice of W_UV (rows
+//     contiguous along the contraction), whose rows each wave then keeps in
+//     registers while it loops over 64-token groups, the next group's o_lat
+//     rows copied while the current one computes.
 #include <algorithm>
 #include <type_traits>
 #include "device_common.hpp"
