@@ -87,6 +87,18 @@ def test_prefill_nope_geometry():
     compare(case, out, lse)
 
 
+def test_prefill_two_heads():
+    # 2 heads: the stacked [W_UK; W_UV] is 384 + 512 rows, seven 128-row weight
+    # tiles, a single XCD group, so most of the decompression's workgroups have
+    # no tile and leave at once.
+    s = spec("glm52_causal_tq4", name="pf_h2", n_head=2, batch=2, t_q=33, seq_len=0, fixed_lens=(300, 77),
+             max_blocks=20, spare_blocks=3)
+    case = mi.make_case(s)
+    out, lse, status = run_prefill(case)
+    assert status == 0
+    compare(case, out, lse)
+
+
 def test_prefill_f32_output_and_edge_requests():
     # Request 1 is empty (zeros, -inf); request 2 is shorter than t_q (NaN and a status bit).
     s = spec("glm52_causal_tq4", name="pf_edge", batch=4, t_q=20, seq_len=0, fixed_lens=(45, 0, 7, 20),
