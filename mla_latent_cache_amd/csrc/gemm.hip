@@ -15,12 +15,13 @@
 // rows (whole cache lines), at a pitch of one 16-byte chunk more than the row
 // so that 16 rows' same chunk falls on 16 distinct bank groups; results leave
 // through an LDS stage as whole rows.
-//   * Absorb: one workgroup per head, 64-column slice of W_UK and 64-token
-//     group.  W_UK is contiguous along the output index, so its slice is read
-//     back from LDS with the transposing ds_read_b64_tr_b16.  The token groups
-//     of one (head, slice) sit on one XCD (grid z is the slowest index and
-//     H x slices is a multiple of 8 at the usual sizes), so their weight reads
-//     after the first come from that XCD's L2.
+//   * Absorb: one workgroup per head and 64-column slice of W_UK, with the
+//     64-token groups spread over grid z only as far as those workgroups
+//     leave compute units idle.  W_UK is contiguous along the output index,
+//     so its slice is read back from LDS with the transposing
+//     ds_read_b64_tr_b16.  absorb_mfma serves one group per workgroup in a
+//     single pass; absorb_loop serves several, with the slice read once and
+//     the next group's rows copied while the current one computes.
 //   * Decompress: one workgroup per head and 64-row slice of W_UV (rows
 //     contiguous along the contraction), whose rows each wave then keeps in
 //     registers while it loops over 64-token groups, the next group's o_lat
@@ -272,6 +273,121 @@ __global__ __launch_bounds__(256) void absorb_mfma(int H, int R, int kv_rank, in
   }
 }
 
+// Absorb for workgroups that serve several token groups of one (head,
+// column slice): the weight slice is copied once and kept as the A operand
+// in registers, its LDS buffer then takes token rows, and each group's
+// q_nope rows are copied into one of two buffers while the previous group
+// computes.  (With one group per workgroup the single-pass kernel above is
+// faster by a few tenths of a microsecond.)
+template <typename TO, int KS>
+__global__ __launch_bounds__(256) void absorb_loop(int H, int R, int kv_rank, int n_tok,
+                                                   const uint16_t* __restrict__ q_nope,
+                                                   const uint16_t* __restrict__ q_pe,
+                                                   const uint16_t* __restrict__ w_uk,
+                                                   TO* __restrict__ q_abs) {
+  constexpr int DN = 32 * KS, NTW = absorb_tiles<KS>(), P = 4 * KS + 1, G = 16 * NTW;
+  constexpr int kTokSlots = (G * P + 63) / 64 * 64;
+  constexpr int kBuf1 = kTokSlots > DN * 8 ? kTokSlots : DN * 8;
+  __shared__ __attribute__((aligned(16))) u32x4 buf0[kTokSlots];  // token rows, pitch P chunks
+  __shared__ __attribute__((aligned(16))) u32x4 buf1[kBuf1];      // the weight slice (swizzled), then token rows
+  __shared__ __attribute__((aligned(16))) u32x4 ol[G * stage_pitch<TO>()];
+  const int h = blockIdx.x, c0 = blockIdx.y * kCols, zs = (int)gridDim.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const int D = kv_rank + R;
+  const int ngroups = (n_tok + G - 1) / G;
+  const uint32_t qpitch = (uint32_t)(H * DN * 2);
+
+  // The q_nope rows of group gi into LDS buffer b.
+  auto copy_group = [&](int gi, int b) {
+    const int m0 = gi * G, cnt = min(G, n_tok - m0);
+    copy_rows<4 * KS>(raw_rsrc(q_nope + ((int64_t)m0 * H + h) * DN, (uint32_t)(cnt - 1) * qpitch + DN * 2),
+                      lds_addr(b ? buf1 : buf0), cnt, qpitch, w, lane);
+  };
+  // Weight slice W_UK[h][0:DN][c0:c0+64] into buffer 1: eight rows (1 KB) per copy, copy i by wave i % 4.
+  const i32x4 wrs = raw_rsrc(w_uk + (int64_t)h * DN * kv_rank, (uint32_t)(DN * kv_rank * 2));
+  const uint32_t wbase = lds_addr(buf1);
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    const int i = w + 4 * u;
+    const int row = 8 * i + (lane >> 3);
+    dma16(wrs, wbase + 1024u * i, (uint32_t)(row * kv_rank + c0 + 8 * ((lane & 7) ^ chunk_swz(row))) * 2u);
+  }
+  int gi = (int)blockIdx.z;  // < ngroups: the launch has at most ngroups z-slices
+  copy_group(gi, 0);
+
+  // Rope columns, dealt over the head's column slices in 16-byte pieces (or
+  // element by element for a rope width that is not a multiple of 8): this
+  // thread's first piece of a group is loaded with the group's copies and
+  // stored as soon as they have landed.
+  const int r8 = R >> 3;
+  const int q_step = 256 * (int)gridDim.y, q_first = (int)blockIdx.y * 256 + tid;
+  auto rope_src = [&](int m0, int qi) { return q_pe + ((int64_t)(m0 + qi / r8) * H + h) * R + 8 * (qi % r8); };
+  auto rope_put = [&](int m0, int qi, u32x4 v) {
+    TO* dst = q_abs + ((int64_t)(m0 + qi / r8) * H + h) * D + kv_rank + 8 * (qi % r8);
+    if constexpr (sizeof(TO) == 2) {
+      *reinterpret_cast<u32x4*>(dst) = v;
+    } else {
+      const bf16x8 x = as_bf16x8(v);
+      *reinterpret_cast<f32x4*>(dst) = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+    }
+  };
+  auto rope_pieces = [&](int gi) { return (R & 7) == 0 ? min(G, n_tok - gi * G) * r8 : 0; };
+  u32x4 qv = {0u, 0u, 0u, 0u};
+  if (q_first < rope_pieces(gi)) qv = *reinterpret_cast<const u32x4*>(rope_src(gi * G, q_first));
+  wait_vmcnt<0>();
+  if (q_first < rope_pieces(gi)) rope_put(gi * G, q_first, qv);
+  barrier_keep_loads();
+
+  // This wave's 16 weight columns as the A operand: lane (l16, g) of k-step t
+  // holds column 16 w + l16, rows 32 t + 8 g .. + 7 (two transposing reads).
+  const char* wlb = reinterpret_cast<const char*>(buf1);
+  bf16x8 A[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    const int prow = 32 * t + 8 * g + (l16 >> 2);
+    const int chunk = 2 * w + ((l16 & 3) >> 1), half = 8 * (l16 & 1);
+    const s16x4 b0 = lds_read_tr16(wlb + prow * 128 + (chunk ^ chunk_swz(prow)) * 16 + half);
+    const s16x4 b1 = lds_read_tr16(wlb + (prow + 4) * 128 + (chunk ^ chunk_swz(prow + 4)) * 16 + half);
+    A[t] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  if (gi + zs < ngroups) barrier_keep_loads();  // every wave holds its weights: buffer 1 is free
+
+  for (int b = 0; gi < ngroups; gi += zs, b ^= 1) {
+    const int m0 = gi * G, cnt = min(G, n_tok - m0);
+    const int nt = (cnt + 15) / 16;
+    const bool more = gi + zs < ngroups;
+    const bool next_piece = more && q_first < rope_pieces(gi + zs);
+    if (more) copy_group(gi + zs, b ^ 1);
+    if (next_piece) qv = *reinterpret_cast<const u32x4*>(rope_src((gi + zs) * G, q_first));
+    dispatch_tiles<NTW>(nt, [&](auto nt_c) {
+      constexpr int NT = decltype(nt_c)::value;
+      f32x4 acc[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tile_products<NT, KS, P>(acc, A, (b ? buf1 : buf0) + l16 * P + g);
+      stage_tiles<TO, NT>(ol, acc, w, l16, g);
+    });
+    if (more) wait_vmcnt<0>();  // the next group's rows (and this wave's earlier stores)
+    if (next_piece) rope_put((gi + zs) * G, q_first, qv);
+    barrier_keep_loads();  // stage complete; the next group's rows visible; buffer b free
+    store_rows<TO>(ol, cnt, kCols, D % 8 == 0,
+                   [&](int r) { return q_abs + ((int64_t)(m0 + r) * H + h) * D + c0; }, tid);
+
+    const int pieces = rope_pieces(gi);
+    for (int qi = q_first + q_step; qi < pieces; qi += q_step)
+      rope_put(m0, qi, *reinterpret_cast<const u32x4*>(rope_src(m0, qi)));
+    if ((R & 7) != 0) {
+      for (int idx = q_first; idx < cnt * R; idx += q_step) {
+        const int n = idx / R, r = idx - n * R;
+        store_c(q_abs, ((int64_t)(m0 + n) * H + h) * D + kv_rank + r,
+                bf16_to_f32(q_pe[((int64_t)(m0 + n) * H + h) * R + r]));
+      }
+    }
+    if (more) barrier_keep_loads();  // the stage is read out before the next group writes it
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decompress, bf16 weights.  Grid (n_head, ceil(d_v / 64), zs); 256 threads;
 // kv_rank = 32 KS.  The workgroup copies its 64 rows of W_UV[h] (rows past
@@ -432,14 +548,29 @@ hipError_t launch_absorb(int H, int DN, int R, int KR, int64_t n_tok, const void
                    *wk = static_cast<const uint16_t*>(w_uk);
     with_ksteps(DN / 32, [&](auto ks_c) {
       constexpr int KS = decltype(ks_c)::value;
+      // Token groups are spread over grid z only as far as the (head, column
+      // slice) workgroups leave compute units idle; where a workgroup is left
+      // with several groups it loops over them and reads its weight slice into
+      // LDS once.
       const int per = 16 * absorb_tiles<KS>();
-      const dim3 grid(H, KR / kCols, (unsigned)((n_tok + per - 1) / per));
-      if (out_bf16)
-        hipLaunchKernelGGL((absorb_mfma<uint16_t, KS>), grid, dim3(256), 0, stream, H, R, KR, (int)n_tok, qn, qp,
-                           wk, static_cast<uint16_t*>(q_abs));
-      else
-        hipLaunchKernelGGL((absorb_mfma<float, KS>), grid, dim3(256), 0, stream, H, R, KR, (int)n_tok, qn, qp, wk,
-                           static_cast<float*>(q_abs));
+      const int64_t groups = (n_tok + per - 1) / per, slices = (int64_t)H * (KR / kCols);
+      const int64_t zs = std::max<int64_t>(1, std::min<int64_t>(groups, 256 / std::max<int64_t>(1, slices)));
+      const dim3 grid(H, KR / kCols, (unsigned)zs);
+      if (zs == groups) {
+        if (out_bf16)
+          hipLaunchKernelGGL((absorb_mfma<uint16_t, KS>), grid, dim3(256), 0, stream, H, R, KR, (int)n_tok, qn, qp,
+                             wk, static_cast<uint16_t*>(q_abs));
+        else
+          hipLaunchKernelGGL((absorb_mfma<float, KS>), grid, dim3(256), 0, stream, H, R, KR, (int)n_tok, qn, qp,
+                             wk, static_cast<float*>(q_abs));
+      } else {
+        if (out_bf16)
+          hipLaunchKernelGGL((absorb_loop<uint16_t, KS>), grid, dim3(256), 0, stream, H, R, KR, (int)n_tok, qn, qp,
+                             wk, static_cast<uint16_t*>(q_abs));
+        else
+          hipLaunchKernelGGL((absorb_loop<float, KS>), grid, dim3(256), 0, stream, H, R, KR, (int)n_tok, qn, qp,
+                             wk, static_cast<float*>(q_abs));
+      }
     });
     return hipGetLastError();
   }
