@@ -134,6 +134,11 @@ GEMM_GEOMS = {
     "ks16_nope": (4, 512, 0, 64, 512),
     "rope4_dv40": (4, 64, 4, 40, 128),
     "ks1_rope12": (3, 32, 12, 36, 64),
+    # 256 or more (head, column slice) workgroups: absorb loops over the token
+    # groups in one workgroup from 65 tokens on (rope copied element by
+    # element; no rope with the longest contraction).
+    "loop_rope12": (64, 32, 12, 36, 256),
+    "loop_ks16_nope": (32, 512, 0, 64, 512),
 }
 
 
